@@ -1,0 +1,278 @@
+"""Seeded workloads for sparse FP8 MLA decode over an ``fp8_ds_mla`` cache.
+
+Cache format (vLLM PR #52212 and SGLang PR #26208 pages; SGLang page,
+"key source snippets", the DSV4 constants and the gather+dequant kernel):
+
+* a row is 576 data bytes: 448 FP8-E4M3 NoPE bytes then 64 bf16 RoPE values
+  (128 bytes, little endian), plus 8 scale bytes: 7 UE8M0 codes, one per 64
+  NoPE dims, and one pad byte;
+* a page of ``block_size`` rows keeps the data rows first and the scale
+  words in a separate region after them:
+  ``page*page_stride + off*576`` (data), ``page*page_stride + bs*576 + off*8``
+  (scales).
+
+Value recipe (one reading of the spec description, the same for all
+configurations): NoPE = E4M3FN(round-to-nearest-even(clamp(N(0,1) / 2^(c-127),
++-448))) with codes c uniform in [120, 130]; RoPE = bf16(N(0,1)); q =
+bf16(N(0,1)); sink logits fp32 N(0,1); softmax scale fp32(512^-0.5).
+
+Only cache rows that some index list references get data.  Every other byte
+of the pool (unreferenced slots, slots past a sequence's length, slack pages)
+holds 0xFF, which decodes to NaN in every field, so a kernel that reads a row
+it should not read cannot go unnoticed.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+D_QK = 512
+D_NOPE = 448
+D_ROPE = 64
+ROW_DATA_BYTES = 576
+ROW_SCALE_BYTES = 8
+ROW_BYTES = ROW_DATA_BYTES + ROW_SCALE_BYTES
+FP8_E4M3_MAX = 448.0
+POISON = 0xFF
+
+# The five decode workloads.  ``seq_len`` is ("fixed", L) or
+# ("loguniform", lo, hi); ``invalid_frac`` is the share of main top-k
+# positions set to -1; ``valid_len`` is None or an inclusive (lo, hi) range
+# for the per-row length of the main list.
+CONFIGS = [
+    dict(name="tiny", B=1, H=16, topk=128, swa=0, seq_len=("fixed", 2048),
+         invalid_frac=0.05, valid_len=None, num_splits=1),
+    dict(name="short_batch", B=4, H=64, topk=512, swa=128, seq_len=("fixed", 8192),
+         invalid_frac=0.02, valid_len=None, num_splits=0),
+    dict(name="long_lowbatch", B=1, H=64, topk=2048, swa=0, seq_len=("fixed", 131072),
+         invalid_frac=0.01, valid_len=None, num_splits=0),
+    dict(name="large_batch", B=256, H=64, topk=512, swa=128, seq_len=("fixed", 8192),
+         invalid_frac=0.0, valid_len=None, num_splits=0),
+    dict(name="ragged", B=32, H=128, topk=2048, swa=128, seq_len=("loguniform", 1024, 65536),
+         invalid_frac=0.05, valid_len=(1024, 2048), num_splits=0),
+]
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    seed: int
+    B: int
+    H: int
+    topk: int
+    swa: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    page_stride: int
+    seq_lens: np.ndarray          # int64 [B]
+    q: np.ndarray                 # uint16 [B, H, 512], bf16 bit patterns
+    kv: np.ndarray                # uint8 [num_blocks, page_stride]
+    block_table: np.ndarray       # int32 [B, max_blocks_per_seq], -1 = unused
+    topk_idx: np.ndarray          # int32 [B, topk + swa], req-local slots, -1 = invalid
+    valid_len: Optional[np.ndarray]  # int32 [B] or None
+    sink: Optional[np.ndarray]    # float32 [H] or None
+    sm_scale: float               # an exact fp32 value
+    num_splits: int               # 0 = let the library choose
+    # With keep_floats: (seq, slot, codes [n,7], NoPE values before FP8
+    # rounding [n,448] as float32, RoPE values before bf16 rounding [n,64]).
+    source_rows: Optional[tuple] = None
+
+    @property
+    def Kt(self) -> int:
+        return self.topk + self.swa
+
+
+def _fp8_e4m3_bytes(x: np.ndarray) -> np.ndarray:
+    """Round float32 values (already clamped to +-448) to E4M3FN bytes, RNE."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _round_half_up(v: float) -> int:
+    return int(math.floor(v + 0.5))
+
+
+def make_custom(*, B: int, H: int, topk: int, swa: int, seq_lens: Sequence[int],
+                seed: int, block_size: int = 64, invalid_frac: float = 0.0,
+                valid_len_range: Optional[tuple] = None, with_sink: bool = True,
+                page_pad: int = 0, slack_frac: float = 0.02, num_splits: int = 0,
+                poison_masked_rows: bool = False, name: str = "custom",
+                keep_floats: bool = False,
+                rng: Optional[np.random.Generator] = None) -> Workload:
+    """Build one seeded workload.
+
+    ``seq_lens`` gives the slot count of every sequence.  Main indices are
+    drawn uniformly without replacement from each sequence's slots (all of
+    them when the sequence is shorter than ``topk``, the rest -1); exactly
+    round(invalid_frac*topk) main positions are then set to -1; the SWA part
+    is the last ``swa`` slots, ascending.  With ``poison_masked_rows`` the
+    rows that only masked-tail entries (past ``valid_len``) name keep their
+    0xFF poison instead of data.
+    """
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    assert seq_lens.shape == (B,)
+    bs = int(block_size)
+    Kt = topk + swa
+
+    # Pages: one shuffled pool, ceil(L/bs) pages per sequence, slack left poisoned.
+    pages_per_seq = (seq_lens + bs - 1) // bs
+    needed = int(pages_per_seq.sum())
+    pool = needed + int(math.ceil(slack_frac * needed))
+    perm = rng.permutation(pool).astype(np.int64)
+    max_blocks = max(int(pages_per_seq.max()), 1)
+    block_table = np.full((B, max_blocks), -1, dtype=np.int32)
+    cursor = 0
+    for b in range(B):
+        n = int(pages_per_seq[b])
+        block_table[b, :n] = perm[cursor:cursor + n]
+        cursor += n
+
+    # Index lists: [main top-k | SWA], req-local slots.
+    topk_idx = np.full((B, Kt), -1, dtype=np.int32)
+    n_invalid = _round_half_up(invalid_frac * topk)
+    for b in range(B):
+        L = int(seq_lens[b])
+        n = min(topk, L)
+        topk_idx[b, :n] = rng.choice(L, size=n, replace=False)
+        if n_invalid:
+            pos = rng.choice(topk, size=n_invalid, replace=False)
+            topk_idx[b, pos] = -1
+        for j in range(swa):
+            p = L - swa + j
+            topk_idx[b, topk + j] = p if p >= 0 else -1
+
+    valid_len = None
+    if valid_len_range is not None:
+        lo, hi = valid_len_range
+        valid_len = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+
+    q = _bf16_bits(rng.standard_normal((B, H, D_QK), dtype=np.float32))
+    sink = rng.standard_normal(H).astype(np.float32) if with_sink else None
+    sm_scale = float(np.float32(D_QK ** -0.5))
+
+    # Rows for every referenced (sequence, slot) pair, in a fixed order.
+    ref_b, ref_slot = [], []
+    for b in range(B):
+        row = topk_idx[b]
+        keep = row >= 0
+        if poison_masked_rows and valid_len is not None:
+            vl = int(np.clip(valid_len[b], 0, topk))
+            keep = keep & ((np.arange(Kt) < vl) | (np.arange(Kt) >= topk))
+        u = np.unique(row[keep].astype(np.int64))
+        ref_b.append(np.full(u.shape, b, dtype=np.int64))
+        ref_slot.append(u)
+    ref_b = np.concatenate(ref_b) if ref_b else np.zeros(0, np.int64)
+    ref_slot = np.concatenate(ref_slot) if ref_slot else np.zeros(0, np.int64)
+    n_rows = ref_b.shape[0]
+
+    codes = rng.integers(120, 131, size=(n_rows, 7)).astype(np.uint8)
+    nope_n = rng.standard_normal((n_rows, D_NOPE), dtype=np.float32)
+    rope_n = rng.standard_normal((n_rows, D_ROPE), dtype=np.float32)
+    scale = np.exp2(codes.astype(np.float32) - 127.0)
+    nope_x = np.clip(nope_n / np.repeat(scale, 64, axis=1), -FP8_E4M3_MAX, FP8_E4M3_MAX)
+    nope_b = _fp8_e4m3_bytes(nope_x)
+    rope_b = _bf16_bits(rope_n).view(np.uint8).reshape(n_rows, 2 * D_ROPE)
+    data = np.concatenate([nope_b, rope_b], axis=1)  # [n, 576]
+    sc = np.concatenate([codes, np.zeros((n_rows, 1), np.uint8)], axis=1)  # [n, 8]
+
+    page_stride = bs * ROW_BYTES + int(page_pad)
+    kv = np.full((pool, page_stride), POISON, dtype=np.uint8)
+    if n_rows:
+        page = block_table[ref_b, ref_slot // bs].astype(np.int64)
+        off = ref_slot % bs
+        flat = kv.reshape(-1)
+        d0 = page * page_stride + off * ROW_DATA_BYTES
+        s0 = page * page_stride + bs * ROW_DATA_BYTES + off * ROW_SCALE_BYTES
+        flat[d0[:, None] + np.arange(ROW_DATA_BYTES)[None, :]] = data
+        flat[s0[:, None] + np.arange(ROW_SCALE_BYTES)[None, :]] = sc
+
+    return Workload(name=name, seed=seed, B=B, H=H, topk=topk, swa=swa, block_size=bs,
+                    num_blocks=pool, max_blocks_per_seq=max_blocks, page_stride=page_stride,
+                    seq_lens=seq_lens, q=q, kv=kv, block_table=block_table, topk_idx=topk_idx,
+                    valid_len=valid_len, sink=sink, sm_scale=sm_scale, num_splits=num_splits,
+                    source_rows=((ref_b, ref_slot, codes, nope_x.astype(np.float32), rope_n)
+                                 if keep_floats else None))
+
+
+def make_workload(config: int, *, seed: Optional[int] = None, block_size: int = 64,
+                  **overrides) -> Workload:
+    """One of the five decode workloads; seed defaults to 1000 + config."""
+    c = CONFIGS[config]
+    seed = 1000 + config if seed is None else seed
+    rng = np.random.default_rng(seed)
+    kind = c["seq_len"][0]
+    if kind == "fixed":
+        seq_lens = np.full(c["B"], c["seq_len"][1], dtype=np.int64)
+    else:
+        lo, hi = c["seq_len"][1], c["seq_len"][2]
+        u = rng.uniform(math.log(lo), math.log(hi), size=c["B"])
+        seq_lens = np.floor(np.exp(u)).astype(np.int64)
+    kw = dict(B=c["B"], H=c["H"], topk=c["topk"], swa=c["swa"], seq_lens=seq_lens, seed=seed,
+              block_size=block_size, invalid_frac=c["invalid_frac"],
+              valid_len_range=c["valid_len"], num_splits=c["num_splits"], name=c["name"], rng=rng)
+    kw.update(overrides)
+    return make_custom(**kw)
+
+
+def workload_digest(w: Workload) -> str:
+    h = hashlib.sha256()
+    for a in (w.seq_lens, w.q, w.kv, w.block_table, w.topk_idx, w.valid_len, w.sink):
+        if a is not None:
+            h.update(np.ascontiguousarray(a).tobytes())
+    h.update(repr((w.B, w.H, w.topk, w.swa, w.block_size, w.num_blocks, w.page_stride,
+                   w.sm_scale)).encode())
+    return h.hexdigest()
+
+
+@dataclasses.dataclass
+class ConvertCase:
+    req_id: np.ndarray        # int32 [num_tokens]
+    block_table: np.ndarray   # int32 [num_reqs, bt_cols]
+    max_blocks: int           # columns that may be used (<= bt_cols)
+    token_indices: np.ndarray  # int32 [num_tokens, ti_cols]
+    width: int                # columns per token (<= ti_cols)
+    block_size: int
+    cu_seqlens: Optional[np.ndarray]  # int32 [num_tokens + 1] or None
+
+
+def make_convert_case(*, seed: int, num_tokens: int, width: int, block_size: int,
+                      num_reqs: int, max_blocks: int, ragged: bool,
+                      bt_extra_cols: int = 3, ti_extra_cols: int = 5,
+                      bad_frac: float = 0.1) -> ConvertCase:
+    """Inputs for the req-local -> global index conversion with every kind of
+    bad entry mixed in: -1 and other negatives, block numbers past the table,
+    negative page entries, requests outside the table."""
+    rng = np.random.default_rng(seed)
+    bt = rng.integers(0, 1 << 16, size=(num_reqs, max_blocks + bt_extra_cols)).astype(np.int32)
+    holes = rng.random(bt.shape) < bad_frac
+    bt[holes] = -1
+    req = rng.integers(0, num_reqs, size=num_tokens).astype(np.int32)
+    if num_tokens > 2:
+        req[rng.integers(0, num_tokens)] = num_reqs  # one request past the table
+    span = max_blocks * block_size
+    ti = rng.integers(0, span, size=(num_tokens, width + ti_extra_cols)).astype(np.int32)
+    r = rng.random(ti.shape)
+    ti[r < bad_frac] = -1
+    ti[(r >= bad_frac) & (r < 1.5 * bad_frac)] = -7
+    hi = (r >= 1.5 * bad_frac) & (r < 2 * bad_frac)
+    ti[hi] = rng.integers(span, span + 4 * block_size, size=int(hi.sum()))
+    cu = None
+    if ragged:
+        n = rng.integers(0, width + 1, size=num_tokens)
+        cu = np.zeros(num_tokens + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(n)
+    return ConvertCase(req_id=req, block_table=bt, max_blocks=max_blocks, token_indices=ti,
+                       width=width, block_size=block_size, cu_seqlens=cu)

@@ -1,0 +1,262 @@
+"""Pins of the oracle's attention against things other than itself:
+
+* torch's fp64 scaled-dot-product attention (math backend, which also returns
+  the softmax weights) on rows rebuilt from the generator's own values, with
+  the sink as an extra key of zero value whose logit is the sink;
+* closed forms (identical rows, a single entry, no valid entry);
+* invariants (index order, split count, page placement, poison rows never
+  read, weights plus sink mass equal to one).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_custom
+
+RTOL = 1e-10
+ATOL = 1e-12
+
+
+def _bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16) \
+        .to(torch.float64).numpy()
+
+
+def _source_row_table(w):
+    """(seq, slot) -> dequantised row rebuilt from the generator's values:
+    torch rounds the NoPE values to E4M3FN and the RoPE values to bf16."""
+    ref_b, ref_slot, codes, nope_x, rope_f = w.source_rows
+    nope = torch.from_numpy(nope_x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nope = nope * np.repeat(np.exp2(codes.astype(np.float64) - 127.0), 64, axis=1)
+    rope = torch.from_numpy(rope_f).to(torch.bfloat16).to(torch.float64).numpy()
+    rows = np.concatenate([nope, rope], axis=1)
+    return {(int(b), int(s)): rows[i] for i, (b, s) in enumerate(zip(ref_b, ref_slot))}
+
+
+def _entry_mask(w, b):
+    Kt = w.topk + w.swa
+    cols = np.arange(Kt)
+    vl = w.topk if w.valid_len is None else int(np.clip(w.valid_len[b], 0, w.topk))
+    return (w.topk_idx[b] >= 0) & ((cols < vl) | (cols >= w.topk))
+
+
+def sdpa_reference(w, sink_bias_when_none=0.0):
+    """Returns (out, lse) from torch's math-backend SDPA in fp64."""
+    table = _source_row_table(w)
+    B, H, Kt = w.B, w.H, w.topk + w.swa
+    out = np.zeros((B, H, 512))
+    lse = np.zeros((B, H))
+    for b in range(B):
+        m = _entry_mask(w, b)
+        K = np.zeros((Kt + 1, 512))
+        for k in range(Kt):
+            if m[k]:
+                K[k] = table[(b, int(w.topk_idx[b, k]))]
+        bias = np.full((H, Kt + 1), -np.inf)
+        bias[:, :Kt][:, m] = 0.0
+        c = w.sink.astype(np.float64) if w.sink is not None else np.full(H, sink_bias_when_none)
+        bias[:, Kt] = c                          # extra key: zero vector, logit = sink
+        q = torch.from_numpy(_bf16_to_f64(w.q[b]))[None, :, None, :]
+        kk = torch.from_numpy(K)[None, None].expand(1, H, Kt + 1, 512)
+        o, wts = torch.ops.aten._scaled_dot_product_attention_math(
+            q, kk, kk, attn_mask=torch.from_numpy(bias)[None, :, None, :], scale=w.sm_scale)
+        o = o[0, :, 0].numpy()
+        ws = wts[0, :, 0, Kt].numpy()            # weight that went to the extra key
+        if w.sink is not None:
+            out[b] = o
+            lse[b] = c - np.log(ws)
+        else:
+            out[b] = o / (1.0 - ws)[:, None]
+            lse[b] = c + np.log((1.0 - ws) / ws)
+    return out, lse
+
+
+def _w(seed, **kw):
+    base = dict(B=3, H=4, topk=40, swa=8, seq_lens=[500, 90, 41], seed=seed, invalid_frac=0.15,
+                valid_len_range=(10, 40), keep_floats=True)
+    base.update(kw)
+    return make_custom(**base)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("bs", [64, 16, 1])
+def test_matches_sdpa_with_sink(seed, bs):
+    w = _w(seed, block_size=bs)
+    out, lse, _ = oracle.decode_workload(w)
+    ro, rl = sdpa_reference(w)
+    np.testing.assert_allclose(out, ro, rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(lse, rl, rtol=RTOL, atol=ATOL)
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_matches_sdpa_without_sink(seed):
+    w = _w(seed, with_sink=False, valid_len_range=None)
+    out, lse, _ = oracle.decode_workload(w)
+    ro, rl = sdpa_reference(w)
+    np.testing.assert_allclose(out, ro, rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(lse, rl, rtol=RTOL, atol=ATOL)
+
+
+def _one_row_case(seed, K, with_sink=True):
+    """B=1 workload whose list names one slot K times (and -1 elsewhere)."""
+    w = make_custom(B=1, H=3, topk=16, swa=0, seq_lens=[64], seed=seed, keep_floats=True,
+                    with_sink=with_sink)
+    slot = int(w.topk_idx[0, 0])
+    w.topk_idx[0, :] = -1
+    w.topk_idx[0, :K] = slot
+    v = _source_row_table(w)[(0, slot)]
+    q = _bf16_to_f64(w.q[0])
+    s = w.sm_scale * (q @ v)           # [H] logits
+    return w, v, s
+
+
+@pytest.mark.parametrize("K", [1, 2, 7])
+def test_closed_form_identical_rows_with_sink(K):
+    w, v, s = _one_row_case(11 + K, K)
+    out, lse, n = oracle.decode_workload(w)
+    assert n == K
+    sink = w.sink.astype(np.float64)
+    den = K * np.exp(s) + np.exp(sink)
+    np.testing.assert_allclose(out[0], (K * np.exp(s) / den)[:, None] * v[None, :], rtol=1e-12,
+                               atol=1e-14)
+    np.testing.assert_allclose(lse[0], np.log(den), rtol=1e-12, atol=1e-14)
+    if K == 1:  # one entry: weight = sigmoid(s - sink)
+        sig = 1.0 / (1.0 + np.exp(-(s - sink)))
+        np.testing.assert_allclose(out[0], sig[:, None] * v[None, :], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[0], np.logaddexp(s, sink), rtol=1e-12)
+
+
+@pytest.mark.parametrize("K", [1, 5])
+def test_closed_form_no_sink_returns_the_row(K):
+    w, v, s = _one_row_case(21 + K, K, with_sink=False)
+    out, lse, _ = oracle.decode_workload(w)
+    np.testing.assert_allclose(out[0], np.broadcast_to(v, out[0].shape), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(lse[0], s + np.log(K), rtol=1e-13)
+
+
+def test_weights_plus_sink_mass_is_one():
+    w, v, s = _one_row_case(31, 6)
+    out, lse, _ = oracle.decode_workload(w)
+    j = int(np.argmax(np.abs(v)))
+    total_w = out[0, :, j] / v[j]
+    sink_mass = np.exp(w.sink.astype(np.float64) - lse[0])
+    np.testing.assert_allclose(total_w + sink_mass, 1.0, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_all_invalid_row_is_zero(with_sink):
+    w = _w(41, with_sink=with_sink)
+    w.topk_idx[1, :] = -1                 # whole row invalid
+    w.topk_idx[2, : w.topk] = -1          # main invalid, SWA still there
+    out, lse, _ = oracle.decode_workload(w)
+    assert np.all(out[1] == 0.0)
+    if with_sink:
+        assert np.array_equal(lse[1], w.sink.astype(np.float64))
+    else:
+        assert np.all(np.isneginf(lse[1]))
+    assert np.all(np.isfinite(out[2])) and np.any(out[2] != 0)
+
+
+def test_index_order_invariance():
+    w = _w(51)
+    out, lse, _ = oracle.decode_workload(w)
+    rng = np.random.default_rng(0)
+    ti = w.topk_idx.copy()
+    for b in range(w.B):
+        vl = int(np.clip(w.valid_len[b], 0, w.topk))
+        ti[b, :vl] = ti[b, :vl][rng.permutation(vl)]
+        ti[b, vl:w.topk] = ti[b, vl:w.topk][rng.permutation(w.topk - vl)]
+        ti[b, w.topk:] = ti[b, w.topk:][rng.permutation(w.swa)]
+    o2, l2, _ = oracle.decode_workload(w, topk_idx=ti)
+    np.testing.assert_allclose(o2, out, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(l2, lse, rtol=1e-13)
+    # Without valid_len every position may move anywhere.
+    w.valid_len = None
+    out, lse, _ = oracle.decode_workload(w)
+    ti = np.stack([r[rng.permutation(r.size)] for r in w.topk_idx])
+    o3, l3, _ = oracle.decode_workload(w, topk_idx=ti)
+    np.testing.assert_allclose(o3, out, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(l3, lse, rtol=1e-13)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 32, 64])
+def test_split_merge_identity(S):
+    w = _w(61, B=2, topk=48, seq_lens=[700, 33])
+    out, lse, _ = oracle.decode_workload(w)
+    o, l, _ = oracle.decode_workload(w, num_splits=S)
+    np.testing.assert_allclose(o, out, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(l, lse, rtol=1e-12, atol=1e-15)
+
+
+def test_valid_len_semantics():
+    w = _w(71)
+    base_vl = w.valid_len.copy()
+    # valid_len = 0 masks the whole main list; the same as main entries set to -1.
+    w.valid_len = np.zeros(w.B, np.int32)
+    o0, l0, _ = oracle.decode_workload(w)
+    ti = w.topk_idx.copy()
+    ti[:, :w.topk] = -1
+    o1, l1, _ = oracle.decode_workload(w, topk_idx=ti, valid_len=None)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    # Negative clamps to 0, above topk clamps to topk (== no valid_len).
+    w.valid_len = np.full(w.B, -5, np.int32)
+    o2, l2, _ = oracle.decode_workload(w)
+    assert np.array_equal(o2, o0) and np.array_equal(l2, l0)
+    w.valid_len = np.full(w.B, w.topk + 9, np.int32)
+    o3, l3, _ = oracle.decode_workload(w)
+    o4, l4, _ = oracle.decode_workload(w, valid_len=None)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+    # valid_len = v is the same as setting main[v:] to -1.
+    w.valid_len = base_vl
+    o5, l5, _ = oracle.decode_workload(w)
+    ti = w.topk_idx.copy()
+    for b in range(w.B):
+        ti[b, base_vl[b]:w.topk] = -1
+    o6, l6, _ = oracle.decode_workload(w, topk_idx=ti, valid_len=None)
+    assert np.array_equal(o5, o6) and np.array_equal(l5, l6)
+
+
+def test_duplicates_count_as_a_multiset():
+    w = _w(81, valid_len_range=None)
+    ti = w.topk_idx.copy()
+    ti[:, 1] = ti[:, 0]                   # entry 0 listed twice
+    w.topk_idx = ti
+    out, lse, _ = oracle.decode_workload(w)
+    ro, rl = sdpa_reference(w)
+    np.testing.assert_allclose(out, ro, rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(lse, rl, rtol=RTOL, atol=ATOL)
+
+
+def test_page_placement_invariance():
+    """Moving pages around the pool (and the table with them) changes
+    nothing; an identity table equals a table-free call on pool slots."""
+    w = _w(91, B=1, seq_lens=[700])
+    out, lse, _ = oracle.decode_workload(w)
+    n = int((w.seq_lens[0] + w.block_size - 1) // w.block_size)
+    kv2 = w.kv.copy()
+    kv2[:n] = w.kv[w.block_table[0, :n]]
+    ident = np.arange(w.max_blocks_per_seq, dtype=np.int32)[None, :]
+    o1, l1, _ = oracle.decode_workload(w, kv=kv2, block_table=ident)
+    assert np.array_equal(o1, out) and np.array_equal(l1, lse)
+    o2, l2, _ = oracle.decode_workload(w, kv=kv2, use_block_table=False)
+    assert np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
+def test_poison_rows_are_never_read():
+    """Masked-tail entries re-pointed at poisoned (0xFF) slots, and entries
+    whose block lies past the table, leave the output bit-identical."""
+    w = _w(101, B=1, seq_lens=[900], topk=40)
+    out, lse, _ = oracle.decode_workload(w)
+    used = set(int(x) for x in w.topk_idx[0] if x >= 0)
+    free = [s for s in range(int(w.seq_lens[0])) if s not in used]
+    ti = w.topk_idx.copy()
+    vl = int(w.valid_len[0])
+    for k in range(vl, w.topk):
+        if ti[0, k] >= 0:
+            ti[0, k] = free.pop()
+    ti[0, vl:w.topk][::3] = w.max_blocks_per_seq * w.block_size + 5
+    o2, l2, _ = oracle.decode_workload(w, topk_idx=ti)
+    assert np.all(np.isfinite(o2))
+    assert np.array_equal(o2, out) and np.array_equal(l2, lse)
