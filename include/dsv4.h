@@ -1,0 +1,223 @@
+/*
+ * dsv4.h -- C ABI of the MI355X (gfx950) sparse FP8 MLA decode library.
+ *
+ * The library computes DeepSeek-V4-style sparse MLA decode over an FP8
+ * "fp8_ds_mla" latent KV cache, and the req-local -> global block-table
+ * index conversion that feeds it.  Sources (page titles):
+ *   vLLM PR #52212, gfx950 DSV4 sparse decode kernel page;
+ *   SGLang PR #26208 report, "[AMD] Dsv4/pr2 compressor opt";
+ *   vLLM PR #41217 report, "[ROCm][Deepseek] dsv3.2 further optimization";
+ *   SGLang PR #26383 page (fused no-split-K attention at >= 256 tokens).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing, keeps no pointer after a call returns,
+ *     never synchronises and never throws across this ABI.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream).
+ *   - The return value is a dsv4_status.  On failure nothing was launched
+ *     (except DSV4_ERR_HIP, where a launch failed) and dsv4_last_error()
+ *     describes the problem for the calling thread.
+ *   - Bad data (negative indices, blocks past the table, page entries
+ *     outside the pool, valid_len outside [0, topk]) is masked, never an
+ *     error: such entries simply do not take part.  Bad shapes, strides,
+ *     alignments or NULL required pointers are errors.
+ *   - Given the same arguments (including the split count) results are
+ *     bitwise reproducible: no atomics take part in any sum.
+ */
+#ifndef DSV4_H
+#define DSV4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+
+typedef enum dsv4_status {
+    DSV4_OK = 0,
+    DSV4_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, bad shape/stride/alignment */
+    DSV4_ERR_NOT_SUPPORTED = 2,      /* a head count the kernels have no variant for      */
+    DSV4_ERR_WORKSPACE_TOO_SMALL = 3,
+    DSV4_ERR_HIP = 4                 /* a kernel launch failed; see dsv4_last_error()     */
+} dsv4_status;
+
+/* Human-readable name of a status value (static storage). */
+const char* dsv4_status_string(int status);
+
+/* Message of the last failed call made by this thread ("" if none). */
+const char* dsv4_last_error(void);
+
+/* ------------------------------------------------------- cache geometry */
+
+/* One cache row: 448 FP8-E4M3FN NoPE bytes then 64 little-endian bf16 RoPE
+ * values (576 bytes), plus 8 scale bytes: UE8M0 code g scales NoPE dims
+ * [64g, 64g+64) by 2^(code-127); the eighth byte is padding.  A page of
+ * block_size rows stores the data rows first and the scale words after
+ * them: row `off` of page `page` is at page*page_stride + off*576, its
+ * scales at page*page_stride + block_size*576 + off*8.
+ * (SGLang PR #26208 report, key source snippets: the DSV4 constants and the
+ * gather+dequant address arithmetic.) */
+#define DSV4_D_QK 512
+#define DSV4_D_NOPE 448
+#define DSV4_D_ROPE 64
+#define DSV4_ROW_DATA_BYTES 576
+#define DSV4_ROW_SCALE_BYTES 8
+#define DSV4_MAX_SPLITS 64
+
+/* ------------------------------------------------------------ decode */
+
+typedef struct dsv4_decode_desc {
+    int32_t batch;               /* B: query tokens, one per sequence (s_q = 1), >= 1 */
+    int32_t num_heads;           /* H: multiple of 16, <= 128 (see NOT_SUPPORTED)   */
+    int32_t topk;                /* main entries per token, >= 0                     */
+    int32_t swa;                 /* sliding-window entries per token, >= 0           */
+    int32_t block_size;          /* slots per page, >= 1                             */
+    int32_t max_blocks_per_seq;  /* usable block_table columns (ignored if no table) */
+    int64_t num_blocks;          /* pages in kv_cache, >= 1                          */
+    int64_t block_table_stride;  /* elements between block_table rows                */
+    int64_t page_stride;         /* bytes between pages: >= block_size*584, mult. of 8 */
+    int64_t topk_idx_stride;     /* elements between topk_idx rows; 0 = topk + swa   */
+    float sm_scale;              /* multiplies q.k (never the sink)                  */
+    void* workspace;             /* device scratch for split partials (may be NULL
+                                    when the call needs none)                        */
+    size_t workspace_bytes;      /* its size                                         */
+} dsv4_decode_desc;
+
+/* What a decode call will launch.  Filled on the host; needs no GPU. */
+typedef struct dsv4_plan {
+    int32_t num_splits;          /* S used (forced, or chosen by the selector)       */
+    int32_t heads_per_group;     /* heads one workgroup serves                       */
+    int32_t head_groups;         /* H / heads_per_group                              */
+    int32_t tile_entries;        /* cache rows per pipeline tile                     */
+    int64_t grid_partial;        /* workgroups of the partial kernel                 */
+    int32_t block_partial;       /* threads per partial workgroup                    */
+    int64_t grid_combine;        /* workgroups of the combine kernel (0 if S == 1)   */
+    int32_t block_combine;       /* threads per combine workgroup                    */
+    size_t workspace_bytes;      /* scratch the call needs (0 if S == 1)             */
+    size_t lds_bytes;            /* LDS per partial workgroup                        */
+} dsv4_plan;
+
+/* Plan a decode without launching anything: validates the descriptor
+ * (pointers other than workspace are not looked at) and picks the split
+ * count.  num_splits = 0 lets the selector choose:
+ *   B >= 256                 -> 1 (one workgroup per token already fills the
+ *                               chip; SGLang PR #26383 page, implementation
+ *                               item 3: no split-K at >= 256 tokens);
+ *   otherwise cap = 4 when topk+swa <= 1024 else 32 (vLLM PR #52212 page,
+ *   implementation item 2: cap 4 for short work, up to 32 for long context
+ *   at low batch), and S = clamp(ceil(256 / (B * head_groups)), 1,
+ *   min(cap, ceil((topk+swa)/32))).
+ * A forced num_splits must lie in [1, DSV4_MAX_SPLITS]. */
+int dsv4_sparse_decode_plan(const dsv4_decode_desc* desc, int32_t num_splits, dsv4_plan* plan);
+
+/* Scratch bytes a decode with this descriptor and split request needs
+ * (0 when S = 1).  Returns 0 also for an invalid descriptor. */
+size_t dsv4_sparse_decode_workspace_bytes(const dsv4_decode_desc* desc, int32_t num_splits);
+
+/* Sparse FP8 MLA decode with an attention sink.
+ *
+ * For token b and head h, entry k of topk_idx row b (columns [0, topk) are
+ * the main list, [topk, topk+swa) the sliding window) takes part iff
+ *   idx = topk_idx[b, k] >= 0, and
+ *   k >= topk, or valid_len is NULL, or k < clamp(valid_len[b], 0, topk), and
+ *   its page resolves: with a block table, idx/block_size <
+ *   max_blocks_per_seq and page = block_table[b, idx/block_size] lies in
+ *   [0, num_blocks); without one (block_table NULL), idx is a pool slot and
+ *   page = idx/block_size must be < num_blocks.  The offset is idx%block_size.
+ * With v_k the dequantised 512-wide row and s_k = sm_scale * q[b,h,:].v_k:
+ *   out[b,h,:] = sum_k e^{s_k - lse} v_k,
+ *   lse[b,h]   = ln(sum_k e^{s_k} + e^{sink[h]})   (natural log; the sink
+ *                term is absent when sink is NULL).
+ * A (b,h) with no taking-part entry gets out = 0 and lse = sink[h], or
+ * -inf without a sink.  Entries are counted as a multiset (duplicates
+ * count twice).  (vLLM PR #52212 page, implementation item 1: one 512-wide
+ * QK dot over NoPE+RoPE, masked tail, attention sink and invalid-index
+ * semantics; SGLang PR #26208 report, gather+dequant kernel: -1 is invalid
+ * and entries at or past the top-k length are masked; unified kernel:
+ * output and LSE with an attention sink.)
+ *
+ * Arguments (all device pointers, caller-owned):
+ *   q          bf16 [B, H, 512], contiguous, 16-byte aligned; q[...,j]
+ *              pairs with row dim j (448 NoPE then 64 RoPE)
+ *   kv_cache   uint8 [num_blocks, page_stride], 8-byte aligned
+ *   block_table int32 [B, block_table_stride] or NULL
+ *   topk_idx   int32 [B, topk_idx_stride], columns [0, topk+swa) used
+ *   valid_len  int32 [B] or NULL
+ *   sink       float [H] or NULL
+ *   out        bf16 [B, H, 512], contiguous, 16-byte aligned
+ *   lse        float [B, H] or NULL (not written)
+ *   num_splits 0 = selector, else the split count to use
+ * The split count changes results only by rounding; with S > 1 the call
+ * needs desc->workspace of at least dsv4_sparse_decode_workspace_bytes().
+ * Launches the partial kernel and, when S > 1, the combine kernel. */
+int dsv4_sparse_decode(const dsv4_decode_desc* desc, const void* q, const void* kv_cache,
+                       const int32_t* block_table, const int32_t* topk_idx,
+                       const int32_t* valid_len, const float* sink, void* out, float* lse,
+                       int32_t num_splits, hipStream_t stream);
+
+/* First stage of dsv4_sparse_decode alone.  With S = 1 it writes out/lse
+ * directly (the same bytes dsv4_sparse_decode writes).  With S > 1 it
+ * writes, for every (b, h, split), the split's normalised partial output
+ * and its log-sum-exp without the sink, into the workspace:
+ *   part_out = (float*)workspace            [B, H, S, 512]
+ *   part_lse = part_out + B*H*S*512         [B, H, S]
+ * A split with no taking-part entry writes 0 and -inf.  Splits cover the
+ * row's effective list main[0:valid_len] ++ swa in contiguous chunks
+ * (vLLM PR #52212 page, implementation item 2: per-row active splits under
+ * a fixed grid). */
+int dsv4_sparse_decode_partial(const dsv4_decode_desc* desc, const void* q,
+                               const void* kv_cache, const int32_t* block_table,
+                               const int32_t* topk_idx, const int32_t* valid_len,
+                               const float* sink, void* out, float* lse, int32_t num_splits,
+                               hipStream_t stream);
+
+/* Merge S split partials with the sink by log-sum-exp:
+ *   M = max(max_s part_lse[b,h,s], sink[h]),
+ *   D = sum_s e^{part_lse - M} + e^{sink[h] - M},
+ *   out[b,h,:] = sum_s e^{part_lse - M} part_out[b,h,s,:] / D  (bf16, RNE),
+ *   lse[b,h] = M + ln D.
+ * All splits empty: out = 0, lse = sink[h] (or -inf without a sink).
+ * (SGLang PR #26208 report, implementation item 3: split-K over the top-k
+ * axis; vLLM PR #52212 page: the reduce of split partials.)
+ *   part_out float [B, H, S, 512], part_lse float [B, H, S] (16-byte aligned),
+ *   sink float [H] or NULL, out bf16 [B, H, 512], lse float [B, H] or NULL.
+ * Also serves partials computed elsewhere (e.g. on other GPUs). */
+int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
+                        const float* part_out, const float* part_lse, const float* sink,
+                        void* out, float* lse, hipStream_t stream);
+
+/* ------------------------------------------------- index conversion */
+
+/* Req-local -> global slot conversion through a block table.  For token t
+ * (request r = req_id[t], or t when req_id is NULL) and column i:
+ *   idx = token_indices[t*ti_stride + i];
+ *   fill when idx < 0, r outside [0, num_reqs), idx/block_size >=
+ *   max_blocks_per_req, page = block_table[r*bt_stride + idx/block_size] < 0,
+ *   or page*block_size + idx%block_size > INT32_MAX (computed in 64 bits);
+ *   otherwise page*block_size + idx%block_size.
+ * Dense (cu_seqlens NULL): out[t*width + i] for i < width.
+ * Ragged: out[cu_seqlens[t] + i] for i < min(cu_seqlens[t+1]-cu_seqlens[t],
+ * width) and inside [0, cu_seqlens[num_tokens]); nothing else is written.  invalid_fill = 0 reproduces the page's
+ * kernel; -1 feeds dsv4_sparse_decode with block_table = NULL.
+ * (vLLM PR #41217 report, key source snippets: the req-index to
+ * global-index kernel, its ragged store from seq_start and block range
+ * check.)  Bit-exact integer work.
+ *   req_id int32 [num_tokens] or NULL; block_table int32 [num_reqs, bt_stride];
+ *   token_indices int32 [num_tokens, ti_stride]; cu_seqlens int32
+ *   [num_tokens+1] or NULL; out int32 as above. */
+int dsv4_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
+                                     const int32_t* block_table, int64_t bt_stride,
+                                     int32_t max_blocks_per_req, const int32_t* token_indices,
+                                     int64_t ti_stride, int32_t num_tokens, int32_t width,
+                                     int32_t block_size, const int32_t* cu_seqlens,
+                                     int32_t invalid_fill, int32_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSV4_H */

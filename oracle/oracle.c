@@ -359,6 +359,7 @@ void orc_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
                     }
                 }
             }
+            if (cu_seqlens && (base + i < 0 || base + i >= cu_seqlens[num_tokens])) continue;
             out[base + i] = (int32_t)v;
         }
     }

@@ -1,0 +1,329 @@
+// Host side of the C ABI declared in include/dsv4.h: argument validation,
+// the split selector, workspace layout and kernel launches.  Nothing here
+// allocates, synchronises or throws; plan and workspace queries make no HIP
+// call at all, so they run on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "dsv4.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return DSV4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Shape {
+    int hg;       // heads per workgroup
+    int groups;   // head groups
+    int splits;   // S
+    int64_t kt;   // topk + swa
+    int64_t idx_stride;
+};
+
+// Validates the descriptor and picks S.  want_ws: also check the workspace.
+int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_plan* plan) {
+    using namespace dsv4;
+    if (!d) return fail(DSV4_ERR_INVALID_ARGUMENT, "desc is NULL");
+    if (d->batch < 1) return fail(DSV4_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", d->batch);
+    if (d->num_heads < 16 || d->num_heads > 128 || d->num_heads % 16)
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "num_heads must be a multiple of 16 in [16, 128] (got %d)", d->num_heads);
+    if (d->topk < 0 || d->swa < 0)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "topk and swa must be >= 0 (got %d, %d)", d->topk,
+                    d->swa);
+    const int64_t kt = (int64_t)d->topk + d->swa;
+    if (kt < 1 || kt > (1 << 24))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "topk + swa must lie in [1, 2^24] (got %lld)",
+                    (long long)kt);
+    if (d->block_size < 1)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "block_size must be >= 1 (got %d)", d->block_size);
+    if (d->num_blocks < 1)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "num_blocks must be >= 1");
+    if (d->page_stride < (int64_t)d->block_size * kRowBytes || d->page_stride % 8)
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "page_stride must be a multiple of 8 and >= block_size*584 = %lld (got %lld)",
+                    (long long)d->block_size * kRowBytes, (long long)d->page_stride);
+    if (d->num_blocks > INT64_MAX / d->page_stride)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "num_blocks * page_stride overflows");
+    const int64_t idx_stride = d->topk_idx_stride == 0 ? kt : d->topk_idx_stride;
+    if (idx_stride < kt)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "topk_idx_stride %lld < topk + swa %lld",
+                    (long long)idx_stride, (long long)kt);
+
+    const int groups = (int)ceil_div(d->num_heads, kMaxHeadsPerGroup);
+    const int hg = d->num_heads / groups;
+    if (hg * groups != d->num_heads || hg % 16)
+        return fail(DSV4_ERR_NOT_SUPPORTED,
+                    "num_heads %d cannot be cut into equal groups of a multiple of 16 heads "
+                    "(at most %d)", d->num_heads, kMaxHeadsPerGroup);
+
+    int S;
+    if (num_splits == 0) {
+        if (d->batch >= 256) {
+            S = 1;
+        } else {
+            const int64_t cap = kt <= 1024 ? 4 : 32;
+            int64_t want = ceil_div(kCUs, (int64_t)d->batch * groups);
+            const int64_t lim = cap < ceil_div(kt, kTile) ? cap : ceil_div(kt, kTile);
+            if (want > lim) want = lim;
+            if (want < 1) want = 1;
+            S = (int)want;
+        }
+    } else if (num_splits < 1 || num_splits > kMaxSplits) {
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "num_splits must be 0 (auto) or in [1, %d] (got %d)",
+                    kMaxSplits, num_splits);
+    } else {
+        S = num_splits;
+    }
+    const int64_t units = (int64_t)d->batch * S;
+    const int64_t grid = ceil_div(units, kXcds) * kXcds * groups;
+    if (grid > INT32_MAX) return fail(DSV4_ERR_INVALID_ARGUMENT, "grid too large");
+
+    sh->hg = hg;
+    sh->groups = groups;
+    sh->splits = S;
+    sh->kt = kt;
+    sh->idx_stride = idx_stride;
+    if (plan) {
+        memset(plan, 0, sizeof *plan);
+        plan->num_splits = S;
+        plan->heads_per_group = hg;
+        plan->head_groups = groups;
+        plan->tile_entries = kTile;
+        plan->grid_partial = grid;
+        plan->block_partial = kThreads;
+        plan->grid_combine = S > 1 ? (int64_t)d->batch * d->num_heads : 0;
+        plan->block_combine = S > 1 ? kCombineThreads : 0;
+        plan->workspace_bytes =
+            S > 1 ? (size_t)d->batch * d->num_heads * S * (kD + 1) * sizeof(float) : 0;
+        plan->lds_bytes = lds_bytes_for(hg);
+    }
+    return DSV4_OK;
+}
+
+int check_decode_ptrs(const dsv4_decode_desc* d, const dsv4_plan& plan, const void* q,
+                      const void* kv, const int32_t* bt, const int32_t* idx, void* out) {
+    if (!q || !kv || !idx || !out)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "q, kv_cache, topk_idx and out must not be NULL");
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned");
+    if (!aligned(kv, 8)) return fail(DSV4_ERR_INVALID_ARGUMENT, "kv_cache must be 8-byte aligned");
+    if (!aligned(idx, 4)) return fail(DSV4_ERR_INVALID_ARGUMENT, "topk_idx must be 4-byte aligned");
+    if (bt) {
+        if (d->max_blocks_per_seq < 1)
+            return fail(DSV4_ERR_INVALID_ARGUMENT, "max_blocks_per_seq must be >= 1 with a block table");
+        if (d->block_table_stride < d->max_blocks_per_seq)
+            return fail(DSV4_ERR_INVALID_ARGUMENT, "block_table_stride %lld < max_blocks_per_seq %d",
+                        (long long)d->block_table_stride, d->max_blocks_per_seq);
+    }
+    if (plan.workspace_bytes) {
+        if (!d->workspace)
+            return fail(DSV4_ERR_WORKSPACE_TOO_SMALL, "num_splits = %d needs a workspace of %zu bytes",
+                        plan.num_splits, plan.workspace_bytes);
+        if (d->workspace_bytes < plan.workspace_bytes)
+            return fail(DSV4_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu",
+                        d->workspace_bytes, plan.workspace_bytes);
+        if (!aligned(d->workspace, 16))
+            return fail(DSV4_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    }
+    return DSV4_OK;
+}
+
+dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const void* q,
+                               const void* kv, const int32_t* bt, const int32_t* idx,
+                               const int32_t* valid_len, const float* sink, void* out, float* lse) {
+    dsv4::DecodeParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.kv = static_cast<const uint8_t*>(kv);
+    p.bt = bt;
+    p.idx = idx;
+    p.valid_len = valid_len;
+    p.sink = sink;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    const size_t n_part = (size_t)d->batch * d->num_heads * sh.splits * dsv4::kD;
+    p.part_o = sh.splits > 1 ? static_cast<float*>(d->workspace) : nullptr;
+    p.part_lse = sh.splits > 1 ? static_cast<float*>(d->workspace) + n_part : nullptr;
+    p.num_blocks = d->num_blocks;
+    p.bt_stride = d->block_table_stride;
+    p.page_stride = d->page_stride;
+    p.idx_stride = sh.idx_stride;
+    p.units = (int64_t)d->batch * sh.splits;
+    p.B = d->batch;
+    p.H = d->num_heads;
+    p.topk = d->topk;
+    p.swa = d->swa;
+    p.bs = d->block_size;
+    p.max_blocks = bt ? d->max_blocks_per_seq : 0;
+    p.S = sh.splits;
+    p.G = sh.groups;
+    p.qk_scale_log2 = d->sm_scale * 1.4426950408889634f;
+    return p;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(DSV4_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const int32_t* bt,
+                const int32_t* idx, const int32_t* valid_len, const float* sink, void* out,
+                float* lse, int32_t num_splits, hipStream_t stream, bool with_combine) {
+    Shape sh;
+    dsv4_plan plan;
+    int st = make_plan(d, num_splits, &sh, &plan);
+    if (st) return st;
+    st = check_decode_ptrs(d, plan, q, kv, bt, idx, out);
+    if (st) return st;
+    const dsv4::DecodeParams p = make_params(d, sh, q, kv, bt, idx, valid_len, sink, out, lse);
+    (void)hipGetLastError();   // start from a clean error state
+    st = launched(dsv4::launch_decode_partial(p, sh.hg, plan.grid_partial, stream), "decode partial");
+    if (st || !with_combine || sh.splits == 1) return st;
+    dsv4::CombineParams c;
+    c.part_o = p.part_o;
+    c.part_lse = p.part_lse;
+    c.sink = sink;
+    c.out = p.out;
+    c.lse = lse;
+    c.B = d->batch;
+    c.H = d->num_heads;
+    c.S = sh.splits;
+    return launched(dsv4::launch_combine(c, stream), "combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsv4_status_string(int status) {
+    switch (status) {
+        case DSV4_OK: return "DSV4_OK";
+        case DSV4_ERR_INVALID_ARGUMENT: return "DSV4_ERR_INVALID_ARGUMENT";
+        case DSV4_ERR_NOT_SUPPORTED: return "DSV4_ERR_NOT_SUPPORTED";
+        case DSV4_ERR_WORKSPACE_TOO_SMALL: return "DSV4_ERR_WORKSPACE_TOO_SMALL";
+        case DSV4_ERR_HIP: return "DSV4_ERR_HIP";
+        default: return "DSV4_ERR_UNKNOWN";
+    }
+}
+
+const char* dsv4_last_error(void) { return g_last_error.c_str(); }
+
+int dsv4_sparse_decode_plan(const dsv4_decode_desc* desc, int32_t num_splits, dsv4_plan* plan) {
+    Shape sh;
+    if (!plan) return fail(DSV4_ERR_INVALID_ARGUMENT, "plan is NULL");
+    const int st = make_plan(desc, num_splits, &sh, plan);
+    return st ? st : ok();
+}
+
+size_t dsv4_sparse_decode_workspace_bytes(const dsv4_decode_desc* desc, int32_t num_splits) {
+    Shape sh;
+    dsv4_plan plan;
+    if (make_plan(desc, num_splits, &sh, &plan)) return 0;
+    ok();
+    return plan.workspace_bytes;
+}
+
+int dsv4_sparse_decode(const dsv4_decode_desc* desc, const void* q, const void* kv_cache,
+                       const int32_t* block_table, const int32_t* topk_idx,
+                       const int32_t* valid_len, const float* sink, void* out, float* lse,
+                       int32_t num_splits, hipStream_t stream) {
+    return decode_impl(desc, q, kv_cache, block_table, topk_idx, valid_len, sink, out, lse,
+                       num_splits, stream, true);
+}
+
+int dsv4_sparse_decode_partial(const dsv4_decode_desc* desc, const void* q,
+                               const void* kv_cache, const int32_t* block_table,
+                               const int32_t* topk_idx, const int32_t* valid_len,
+                               const float* sink, void* out, float* lse, int32_t num_splits,
+                               hipStream_t stream) {
+    return decode_impl(desc, q, kv_cache, block_table, topk_idx, valid_len, sink, out, lse,
+                       num_splits, stream, false);
+}
+
+int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
+                        const float* part_out, const float* part_lse, const float* sink,
+                        void* out, float* lse, hipStream_t stream) {
+    if (batch < 1 || num_heads < 1 || num_splits < 1)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "batch, num_heads and num_splits must be >= 1");
+    if ((int64_t)batch * num_heads > INT32_MAX)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "batch * num_heads too large");
+    if (!part_out || !part_lse || !out)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "part_out, part_lse and out must not be NULL");
+    if (!aligned(part_out, 16) || !aligned(out, 8) || !aligned(part_lse, 4))
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "part_out must be 16-byte aligned, out 8-byte aligned");
+    dsv4::CombineParams c;
+    c.part_o = part_out;
+    c.part_lse = part_lse;
+    c.sink = sink;
+    c.out = static_cast<uint16_t*>(out);
+    c.lse = lse;
+    c.B = batch;
+    c.H = num_heads;
+    c.S = num_splits;
+    (void)hipGetLastError();
+    return launched(dsv4::launch_combine(c, stream), "combine");
+}
+
+int dsv4_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
+                                     const int32_t* block_table, int64_t bt_stride,
+                                     int32_t max_blocks_per_req, const int32_t* token_indices,
+                                     int64_t ti_stride, int32_t num_tokens, int32_t width,
+                                     int32_t block_size, const int32_t* cu_seqlens,
+                                     int32_t invalid_fill, int32_t* out, hipStream_t stream) {
+    if (num_tokens < 0 || width < 0)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "num_tokens and width must be >= 0");
+    if (num_tokens == 0 || width == 0) return ok();
+    if (width > 65535 * 256) return fail(DSV4_ERR_INVALID_ARGUMENT, "width too large");
+    if (!block_table || !token_indices || !out)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "block_table, token_indices and out must not be NULL");
+    if (block_size < 1) return fail(DSV4_ERR_INVALID_ARGUMENT, "block_size must be >= 1");
+    if (num_reqs < 0 || max_blocks_per_req < 0)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "num_reqs and max_blocks_per_req must be >= 0");
+    if (bt_stride < max_blocks_per_req)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "bt_stride < max_blocks_per_req");
+    if (ti_stride < width) return fail(DSV4_ERR_INVALID_ARGUMENT, "ti_stride < width");
+    dsv4::ConvertParams p;
+    p.req_id = req_id;
+    p.bt = block_table;
+    p.ti = token_indices;
+    p.cu = cu_seqlens;
+    p.out = out;
+    p.bt_stride = bt_stride;
+    p.ti_stride = ti_stride;
+    p.num_reqs = num_reqs;
+    p.max_blocks = max_blocks_per_req;
+    p.num_tokens = num_tokens;
+    p.width = width;
+    p.bs = block_size;
+    p.fill = invalid_fill;
+    (void)hipGetLastError();
+    return launched(dsv4::launch_convert(p, stream), "convert");
+}
+
+}  // extern "C"

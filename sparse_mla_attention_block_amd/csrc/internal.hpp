@@ -1,0 +1,88 @@
+// Internal declarations shared by the host API and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsv4 {
+
+// Row geometry of the fp8_ds_mla cache (SGLang PR #26208 report, key source
+// snippets: D_QK 512 = 448 NoPE + 64 RoPE, 576 data bytes and 8 scale bytes
+// per token).
+constexpr int kD = 512;
+constexpr int kDNope = 448;
+constexpr int kDRope = 64;
+constexpr int kRowData = 576;
+constexpr int kRowScale = 8;
+constexpr int kRowBytes = kRowData + kRowScale;
+
+// Decode kernel shape: 4 waves of 64 lanes, 32 cache rows per tile (the
+// "BK32" tiles of the vLLM PR #52212 page), up to 64 heads per workgroup.
+constexpr int kThreads = 256;
+constexpr int kTile = 32;
+constexpr int kMaxHeadsPerGroup = 64;
+constexpr int kMaxSplits = 64;
+constexpr int kCUs = 256;           // MI355X compute units
+constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin
+constexpr int kCombineThreads = 128;  // 4 output dims per thread
+
+// LDS tile geometry (bf16 elements unless noted); the +8 / +1 pads move
+// consecutive rows onto different banks.
+constexpr int kKnLd = kD + 8;       // row-major K tile  [32][520]
+constexpr int kVtLd = kTile + 8;    // transposed V tile [512][40]
+constexpr int kSLd = kTile + 1;     // scores, fp32      [HG][33]
+constexpr int kPLd = kTile + 8;     // probabilities    [HG][40]
+
+constexpr size_t lds_bytes_for(int hg) {
+    return size_t(kTile) * kKnLd * 2 + size_t(kD) * kVtLd * 2 + size_t(hg) * kSLd * 4 +
+           size_t(hg) * kPLd * 2 + size_t(hg) * 4 * 2 + size_t(kTile) * 8 * 2;
+}
+
+struct DecodeParams {
+    const uint16_t* q;          // bf16 [B, H, 512]
+    const uint8_t* kv;          // pages
+    const int32_t* bt;          // [B, bt_stride] or null
+    const int32_t* idx;         // [B, idx_stride]
+    const int32_t* valid_len;   // [B] or null
+    const float* sink;          // [H] or null
+    uint16_t* out;              // bf16 [B, H, 512] (direct output, S == 1)
+    float* lse;                 // [B, H] or null (direct output, S == 1)
+    float* part_o;              // [B, H, S, 512] (S > 1)
+    float* part_lse;            // [B, H, S] (S > 1)
+    int64_t num_blocks;
+    int64_t bt_stride;
+    int64_t page_stride;
+    int64_t idx_stride;
+    int64_t units;              // B * S
+    int32_t B, H, topk, swa, bs, max_blocks, S, G;
+    float qk_scale_log2;        // sm_scale * log2(e)
+};
+
+struct CombineParams {
+    const float* part_o;
+    const float* part_lse;
+    const float* sink;
+    uint16_t* out;
+    float* lse;
+    int32_t B, H, S;
+};
+
+struct ConvertParams {
+    const int32_t* req_id;
+    const int32_t* bt;
+    const int32_t* ti;
+    const int32_t* cu;
+    int32_t* out;
+    int64_t bt_stride;
+    int64_t ti_stride;
+    int32_t num_reqs, max_blocks, num_tokens, width, bs, fill;
+};
+
+// Kernel launchers (return the launch's hipError_t).
+hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
+                                 hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
+
+}  // namespace dsv4

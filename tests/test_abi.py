@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/dsv4.h declares, plans every workload the way the selector rule
+says, and rejects bad arguments with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mla_attention_block_amd as dsv4
+from synth import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "dsv4.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsv4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_symbols()
+    for want in ("dsv4_sparse_decode", "dsv4_sparse_decode_partial", "dsv4_combine_splits",
+                 "dsv4_convert_req_index_to_global", "dsv4_sparse_decode_plan",
+                 "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dsv4.LIB_PATH)
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_built_for_gfx950_only():
+    data = open(dsv4.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert other not in data
+
+
+def _desc(B, H, topk, swa, bs=64, num_blocks=1000, **kw):
+    d = dict(batch=B, num_heads=H, topk=topk, swa=swa, block_size=bs, num_blocks=num_blocks,
+             page_stride=bs * 584, sm_scale=512 ** -0.5, max_blocks_per_seq=16,
+             block_table_stride=16)
+    d.update(kw)
+    return dsv4.make_desc(**d)
+
+
+def _expected_auto_splits(B, H, Kt):
+    groups = -(-H // 64)
+    if B >= 256:
+        return 1
+    cap = 4 if Kt <= 1024 else 32
+    want = -(-256 // (B * groups))
+    return max(1, min(want, cap, -(-Kt // 32)))
+
+
+@pytest.mark.parametrize("ci", range(5))
+def test_plan_of_each_workload(ci):
+    c = CONFIGS[ci]
+    Kt = c["topk"] + c["swa"]
+    p = dsv4.dsv4_sparse_decode_plan(_desc(c["B"], c["H"], c["topk"], c["swa"]), c["num_splits"])
+    S = c["num_splits"] or _expected_auto_splits(c["B"], c["H"], Kt)
+    assert p.num_splits == S
+    assert p.heads_per_group * p.head_groups == c["H"]
+    assert p.heads_per_group <= 64 and p.heads_per_group % 16 == 0
+    units = c["B"] * S
+    assert p.grid_partial == -(-units // 8) * 8 * p.head_groups
+    assert p.block_partial == 256
+    if S > 1:
+        assert p.workspace_bytes == c["B"] * c["H"] * S * 513 * 4
+        assert p.grid_combine == c["B"] * c["H"]
+    else:
+        assert p.workspace_bytes == 0 and p.grid_combine == 0
+    assert p.lds_bytes <= 160 * 1024
+
+
+def test_selector_values_for_the_five_workloads():
+    got = [dsv4.dsv4_sparse_decode_plan(_desc(c["B"], c["H"], c["topk"], c["swa"]),
+                                        c["num_splits"]).num_splits for c in CONFIGS]
+    assert got == [1, 4, 32, 1, 4]
+
+
+@pytest.mark.parametrize("H,hg,groups", [(16, 16, 1), (32, 32, 1), (48, 48, 1), (64, 64, 1),
+                                          (96, 48, 2), (128, 64, 2)])
+def test_head_grouping(H, hg, groups):
+    p = dsv4.dsv4_sparse_decode_plan(_desc(2, H, 100, 0), 1)
+    assert (p.heads_per_group, p.head_groups) == (hg, groups)
+
+
+def _status(desc, splits=0):
+    with pytest.raises(dsv4.Dsv4Error) as e:
+        dsv4.dsv4_sparse_decode_plan(desc, splits)
+    return e.value.status
+
+
+def test_validation_errors():
+    E = dsv4.DSV4_ERR_INVALID_ARGUMENT
+    assert _status(_desc(0, 64, 10, 0)) == E
+    assert _status(_desc(1, 24, 10, 0)) == E            # not a multiple of 16
+    assert _status(_desc(1, 144, 10, 0)) == E           # more than 128
+    assert _status(_desc(1, 64, 0, 0)) == E             # nothing to attend
+    assert _status(_desc(1, 64, -1, 5)) == E
+    assert _status(_desc(1, 64, 10, 0, bs=0)) == E
+    assert _status(_desc(1, 64, 10, 0, num_blocks=0)) == E
+    assert _status(_desc(1, 64, 10, 0, page_stride=64 * 584 - 8)) == E
+    assert _status(_desc(1, 64, 10, 0, page_stride=64 * 584 + 4)) == E
+    assert _status(_desc(1, 64, 10, 2, topk_idx_stride=11)) == E
+    assert _status(_desc(1, 64, 10, 0), 65) == E
+    assert _status(_desc(1, 64, 10, 0), -1) == E
+    N = dsv4.DSV4_ERR_NOT_SUPPORTED
+    assert _status(_desc(1, 80, 10, 0)) == N             # 2 groups of 40
+    assert _status(_desc(1, 112, 10, 0)) == N
+    assert "num_heads" in dsv4.dsv4_last_error()
+
+
+def test_workspace_bytes():
+    d = _desc(4, 64, 512, 128)
+    assert dsv4.dsv4_sparse_decode_workspace_bytes(d, 1) == 0
+    assert dsv4.dsv4_sparse_decode_workspace_bytes(d, 4) == 4 * 64 * 4 * 513 * 4
+    assert dsv4.dsv4_sparse_decode_workspace_bytes(_desc(0, 64, 1, 0), 4) == 0   # invalid
+
+
+def test_decode_rejects_null_and_missing_workspace_without_touching_the_gpu():
+    d = _desc(1, 64, 100, 0)
+    fake = ctypes.c_void_p(4096)
+    st = dsv4._lib.dsv4_sparse_decode(ctypes.byref(d), None, fake, None, fake, None, None, fake,
+                                      None, 1, None)
+    assert st == dsv4.DSV4_ERR_INVALID_ARGUMENT
+    st = dsv4._lib.dsv4_sparse_decode(ctypes.byref(d), fake, fake, None, fake, None, None, fake,
+                                      None, 4, None)
+    assert st == dsv4.DSV4_ERR_WORKSPACE_TOO_SMALL
+    st = dsv4._lib.dsv4_sparse_decode(ctypes.byref(d), ctypes.c_void_p(4100), fake, None, fake,
+                                      None, None, fake, None, 1, None)
+    assert st == dsv4.DSV4_ERR_INVALID_ARGUMENT          # q misaligned
+    st = dsv4._lib.dsv4_convert_req_index_to_global(None, 1, None, 4, 4, fake, 4, 1, 4, 64, None,
+                                                    -1, fake, None)
+    assert st == dsv4.DSV4_ERR_INVALID_ARGUMENT          # no block table
+    assert dsv4._lib.dsv4_convert_req_index_to_global(None, 1, fake, 4, 4, fake, 4, 0, 4, 64,
+                                                      None, -1, fake, None) == dsv4.DSV4_OK
+    assert dsv4._lib.dsv4_combine_splits(1, 64, 0, fake, fake, None, fake, None, None) == \
+        dsv4.DSV4_ERR_INVALID_ARGUMENT
+    assert dsv4.dsv4_status_string(3) == "DSV4_ERR_WORKSPACE_TOO_SMALL"

@@ -1,0 +1,214 @@
+"""Sparse FP8 MLA decode on the GPU against the fp64 oracle.
+
+Every comparison is element by element on the whole output: |d out| <=
+2e-2 + 1e-2 |out_ref| on the bf16 output and |d lse| <= 1e-3, infinities
+equal.  The five workloads run at full size in the launch configuration the
+benchmark uses (the selector's split count), plus forced split counts and
+edge cases on smaller shapes that still span several tiles and a ragged
+tail.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_custom, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _gh():
+    from tests import gpu_helpers
+    return gpu_helpers
+
+
+def _ref(w, **kw):
+    out, lse, _ = oracle.decode_workload(w, **kw)
+    return out, lse
+
+
+def _check(w, what, **gpu_kw):
+    gh = _gh()
+    print(f"decode {what}: B={w.B} H={w.H} topk={w.topk} swa={w.swa} bs={w.block_size} "
+          f"S={gpu_kw.get('num_splits', w.num_splits)}", flush=True)
+    dw = gh.DeviceWorkload(w)
+    out, lse = gh.gpu_decode(dw, **gpu_kw)
+    ro, rl = _ref(w)
+    gh.assert_decode_close(out, lse, ro, rl, what)
+    return dw, out, lse, ro, rl
+
+
+@pytest.mark.parametrize("ci", range(5))
+def test_workload_full_size(ci):
+    w = make_workload(ci)
+    _check(w, f"workload {ci} {w.name}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 32, 64])
+def test_forced_split_counts(S):
+    w = make_custom(B=3, H=64, topk=300, swa=37, seq_lens=[5000, 400, 90], seed=10 + S,
+                    invalid_frac=0.03, valid_len_range=(150, 300))
+    _check(w, f"S={S}", num_splits=S)
+
+
+@pytest.mark.parametrize("H", [16, 32, 48, 64, 96, 128])
+def test_head_counts(H):
+    w = make_custom(B=2, H=H, topk=200, swa=20, seq_lens=[3000, 700], seed=20 + H,
+                    invalid_frac=0.05, valid_len_range=(100, 200))
+    _check(w, f"H={H}", num_splits=0)
+    _check(w, f"H={H} S=1", num_splits=1)
+
+
+@pytest.mark.parametrize("bs,pad", [(1, 0), (1, 8), (16, 0), (64, 64)])
+def test_block_sizes_and_page_strides(bs, pad):
+    w = make_custom(B=2, H=64, topk=150, swa=16, seq_lens=[2000, 321], seed=30 + bs + pad,
+                    block_size=bs, page_pad=pad, invalid_frac=0.04)
+    _check(w, f"bs={bs} pad={pad}", num_splits=3)
+
+
+def test_without_sink_and_without_lse():
+    gh = _gh()
+    w = make_custom(B=2, H=32, topk=100, swa=0, seq_lens=[900, 900], seed=41, with_sink=False,
+                    invalid_frac=0.1)
+    for S in (1, 4):
+        _check(w, f"no sink S={S}", num_splits=S)
+    dw = gh.DeviceWorkload(w)
+    out, lse = gh.gpu_decode(dw, num_splits=4, want_lse=False)
+    assert np.isnan(lse).all()                       # lse = NULL: never written
+    ro, _ = _ref(w)
+    assert np.all(np.abs(out - ro) <= gh.OUT_ATOL + gh.OUT_RTOL * np.abs(ro))
+
+
+@pytest.mark.parametrize("S", [1, 5])
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_empty_and_all_invalid_rows(S, with_sink):
+    gh = _gh()
+    w = make_custom(B=4, H=16, topk=64, swa=8, seq_lens=[500, 500, 500, 500], seed=50,
+                    with_sink=with_sink, valid_len_range=(0, 64))
+    w.topk_idx[0, :] = -1                            # nothing at all
+    w.topk_idx[1, :64] = -1                          # SWA only
+    w.valid_len[2] = 0                               # main masked by valid_len
+    w.valid_len[3] = -7                              # clamps to 0
+    dw, out, lse, ro, rl = _check(w, f"empty rows S={S} sink={with_sink}", num_splits=S)
+    assert np.all(out[0] == 0.0)
+    if with_sink:
+        assert np.allclose(lse[0], w.sink, atol=1e-6)
+    else:
+        assert np.all(np.isneginf(lse[0]))
+
+
+def test_valid_len_beyond_topk_and_null():
+    gh = _gh()
+    w = make_custom(B=2, H=64, topk=100, swa=30, seq_lens=[800, 800], seed=60,
+                    valid_len_range=(0, 1))
+    w.valid_len[:] = [500, 100]                      # both mean "no masking"
+    dw, out, lse, _, _ = _check(w, "valid_len >= topk", num_splits=2)
+    out2, lse2 = gh.gpu_decode(dw, num_splits=2, valid_len=None)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+@pytest.mark.parametrize("scale", [8.0, 30.0])
+def test_large_logits_rescale_stably(scale):
+    w = make_custom(B=1, H=64, topk=512, swa=0, seq_lens=[4096], seed=70, invalid_frac=0.02)
+    qf = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).float() * scale
+    w.q = qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for S in (1, 8):
+        _check(w, f"q x{scale} S={S}", num_splits=S)
+
+
+@pytest.mark.parametrize("sink_value", [25.0, -25.0])
+def test_dominant_or_negligible_sink(sink_value):
+    w = make_custom(B=2, H=64, topk=128, swa=0, seq_lens=[2000, 2000], seed=80)
+    w.sink[:] = sink_value
+    for S in (1, 4):
+        _check(w, f"sink={sink_value} S={S}", num_splits=S)
+
+
+def test_duplicates_count_twice():
+    w = make_custom(B=2, H=64, topk=96, swa=32, seq_lens=[3000, 96], seed=90)
+    w.topk_idx[0, 10:20] = w.topk_idx[0, 0]
+    _check(w, "duplicates", num_splits=3)
+
+
+def test_poisoned_rows_are_never_read_bitwise():
+    """Masked-tail entries re-pointed at 0xFF rows or past the block table
+    give bit-identical output to the clean run."""
+    gh = _gh()
+    w = make_custom(B=2, H=64, topk=256, swa=64, seq_lens=[6000, 3000], seed=100,
+                    invalid_frac=0.05, valid_len_range=(120, 200))
+    dw = gh.DeviceWorkload(w)
+    for S in (1, 4):
+        clean = gh.gpu_decode(dw, num_splits=S)
+        ti = w.topk_idx.copy()
+        for b in range(w.B):
+            used = set(int(x) for x in ti[b] if x >= 0)
+            free = [s for s in range(int(w.seq_lens[b])) if s not in used]
+            vl = int(w.valid_len[b])
+            for k in range(vl, w.topk):
+                ti[b, k] = free.pop() if k % 3 else w.max_blocks_per_seq * w.block_size + k
+        dirty = gh.gpu_decode(dw, num_splits=S, topk_idx=torch.from_numpy(ti).cuda())
+        assert np.array_equal(clean[0], dirty[0]) and np.array_equal(clean[1], dirty[1])
+
+
+def test_deterministic_bitwise():
+    gh = _gh()
+    w = make_workload(1)
+    dw = gh.DeviceWorkload(w)
+    a = gh.gpu_decode(dw)
+    b = gh.gpu_decode(dw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_stage_entry_points_match_the_fused_call():
+    gh = _gh()
+    w = make_workload(2)
+    dw = gh.DeviceWorkload(w)
+    a = gh.gpu_decode(dw)
+    b = gh.gpu_decode(dw, partial_then_combine=True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_global_slots_after_conversion_match_block_table_path():
+    """convert (fill -1) then decode without a table == decode with the table."""
+    gh = _gh()
+    import sparse_mla_attention_block_amd as dsv4
+    w = make_workload(4)
+    dw = gh.DeviceWorkload(w)
+    a = gh.gpu_decode(dw)
+    gslots = torch.empty_like(dw.idx)
+    dsv4.dsv4_convert_req_index_to_global(None, w.B, dw.bt, w.block_table.shape[1],
+                                          w.max_blocks_per_seq, dw.idx, w.Kt, w.B, w.Kt,
+                                          w.block_size, None, -1, gslots)
+    b = gh.gpu_decode(dw, use_bt=False, topk_idx=gslots)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_side_stream_and_no_overrun():
+    """Runs on a non-default stream; guard bytes around out/lse stay intact."""
+    import sparse_mla_attention_block_amd as dsv4
+    gh = _gh()
+    w = make_custom(B=3, H=64, topk=200, swa=10, seq_lens=[1000, 1000, 1000], seed=110)
+    dw = gh.DeviceWorkload(w)
+    S = 3
+    desc = gh.make_desc(w)
+    nbytes = dsv4.dsv4_sparse_decode_workspace_bytes(desc, S)
+    guard = 4096
+    ws_full = torch.full((nbytes + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = ws_full[guard:guard + nbytes]
+    desc = gh.make_desc(w, workspace=ws)
+    n = w.B * w.H * 512
+    out_full = torch.full((n + 2 * 2048,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse_full = torch.full((w.B * w.H + 2 * 256,), 7.0, dtype=torch.float32, device="cuda")
+    out = out_full[2048:2048 + n].view(w.B, w.H, 512)
+    lse = lse_full[256:256 + w.B * w.H].view(w.B, w.H)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        dsv4.dsv4_sparse_decode(desc, dw.q, dw.kv, dw.bt, dw.idx, dw.vl, dw.sink, out, lse, S, st)
+    st.synchronize()
+    assert torch.all(out_full[:2048] == 7.0) and torch.all(out_full[2048 + n:] == 7.0)
+    assert torch.all(lse_full[:256] == 7.0) and torch.all(lse_full[256 + w.B * w.H:] == 7.0)
+    assert torch.all(ws_full[:guard] == 0x5A) and torch.all(ws_full[guard + nbytes:] == 0x5A)
+    ro, rl = _ref(w)
+    gh.assert_decode_close(out.float().double().cpu().numpy(), lse.double().cpu().numpy(), ro,
+                           rl, "side stream")
