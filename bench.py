@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse FP8 MLA decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch:
+  1. req-local -> global slot conversion through the block table (fill -1),
+  2. the decode partial kernel over the global slots,
+  3. the split combine kernel (when the selector picks S > 1).
+The workload is the long-context low-batch decode: B=1 query token, H=64
+heads, top-k 2048 of 131072 cache slots (block size 64, shuffled pages, 1 %
+invalid), fp8_ds_mla rows, sink logits, softmax scale 512^-0.5.
+
+Cache residency: the timed steps rotate over R replicas of the cache (the
+same bytes at R different addresses, each with its own block table), with R
+chosen so that the rows touched between two uses of one replica exceed twice
+the 256 MB Infinity Cache.  Every step therefore reads its rows from HBM, as
+a decode layer does in a model whose other layers and weights stream through
+the caches in between.  A single-replica (cache-warm) figure is reported
+beside it for context.
+
+The steps are captured once into a HIP graph (through torch.cuda.graph) and
+replayed: a decode step is launch-bound, and serving engines replay decode
+steps from graphs.  Per-kernel average durations come from HIP events around
+graphs of K back-to-back launches of each kernel alone, on the stream the
+kernels run on.
+
+Prints ONE JSON line.  Options: --steps K --warmup W --gpus 1 (more GPUs are
+not supported: the path runs on one GPU) --replicas R --no-cpu-baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attended KV tokens/sec + achieved HBM GB/s, sparse FP8 MLA decode B=1 "
+          "topk=2048 H=64")
+WORKLOAD_CONFIG = 2
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
+INFINITY_CACHE_BYTES = 256 << 20
+ROW_BYTES = 584                   # 576 data + 8 scale bytes per valid entry
+INDEX_BYTES = 4
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to defeat the caches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def _source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "internal.hpp"):
+        with open(os.path.join(ROOT, "sparse_mla_attention_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile(digest: str):
+    """HBM bytes per launch of the partial kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_partial_long_lowbatch_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode path "
+              "is single-GPU; see DESIGN.md for how it would shard.", file=sys.stderr)
+        return 2
+    import torch
+    import sparse_mla_attention_block_amd as dsv4
+    from synth import make_workload
+
+    K, W = args.steps, args.warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(WORKLOAD_CONFIG)
+    B, H, Kt = w.B, w.H, w.Kt
+    nb, stride = w.num_blocks, w.page_stride
+    n_valid_slots = int((w.topk_idx >= 0).sum())   # req-local entries that resolve (all do here)
+
+    # Replicas: the same cache bytes at R addresses.
+    touched = n_valid_slots * (ROW_BYTES + 64)      # data sectors + one scale sector per row
+    R = args.replicas or max(1, math.ceil(2 * INFINITY_CACHE_BYTES / touched))
+    base = torch.from_numpy(w.kv).to(dev)
+    pool = torch.empty((R, nb, stride), dtype=torch.uint8, device=dev)
+    pool.copy_(base.unsqueeze(0).expand(R, nb, stride))
+    del base
+    bt0 = torch.from_numpy(w.block_table.astype(np.int64)).to(dev)
+    offs = (torch.arange(R, device=dev, dtype=torch.int64) * nb).view(R, 1, 1)
+    bt_all = torch.where(bt0.unsqueeze(0) >= 0, bt0.unsqueeze(0) + offs, -1).to(torch.int32)
+    bt_all = bt_all.reshape(R * B, -1).contiguous()
+    maxb = bt_all.shape[1]
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    sink = torch.from_numpy(w.sink).to(dev)
+    gslots = torch.empty((B, Kt), dtype=torch.int32, device=dev)
+    gslots_all = torch.empty((R, B, Kt), dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    desc = dsv4.make_desc(batch=B, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
+                          num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale)
+    plan = dsv4.dsv4_sparse_decode_plan(desc, 0)
+    S = plan.num_splits
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    desc = dsv4.make_desc(batch=B, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
+                          num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale, workspace=ws)
+    part_o, part_l = dsv4.workspace_split_views(ws, B, H, S) if S > 1 else (None, None)
+    kv = pool.view(-1)
+
+    def convert(r, dst):
+        dsv4.dsv4_convert_req_index_to_global(None, B, bt_all[r * B:(r + 1) * B], maxb, maxb, idx,
+                                              Kt, B, Kt, w.block_size, None, -1, dst)
+
+    def partial(slots):
+        dsv4.dsv4_sparse_decode_partial(desc, q, kv, None, slots, None, sink, out, lse, S)
+
+    def combine():
+        if S > 1:
+            dsv4.dsv4_combine_splits(B, H, S, part_o, part_l, sink, out, lse)
+
+    def step(r):
+        convert(r, gslots)
+        partial(gslots)
+        combine()
+
+    for r in range(R):
+        convert(r, gslots_all[r])
+    torch.cuda.synchronize()
+
+    def capture(fn, n, offset=0):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(offset % R)            # warm the stream outside the graph
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn((offset + i) % R)
+        return g
+
+    g_warm = capture(step, W) if W > 0 else None
+    g_main = capture(step, K, offset=W)
+
+    # Warmup, then the timed region: exactly K steps.
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    g_main.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3
+    ms_per_step = wall_ms / K
+    ev_ms_per_step = ev0.elapsed_time(ev1) / K
+
+    # Correctness of the timed launches: every replica holds the same rows, so
+    # the last step's output must equal a fresh single call (same bytes).
+    out_timed = out.clone()
+    lse_timed = lse.clone()
+
+    # Per-kernel average durations: K back-to-back launches of one kernel.
+    def time_graph(g, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()                    # untimed pass
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    kt_conv = time_graph(capture(lambda r: convert(r, gslots), K), K)
+    kt_part = time_graph(capture(lambda r: partial(gslots_all[r]), K), K)
+    kt_comb = time_graph(capture(lambda r: combine(), K), K) if S > 1 else 0.0
+
+    # Cache-warm reference: one replica, same step.
+    g_hot = capture(lambda r: step(0), K)
+    hot_ms_per_step = time_graph(g_hot, K)
+    kt_part_hot = time_graph(capture(lambda r: partial(gslots_all[0]), K), K)
+
+    partial(gslots_all[0])
+    combine()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out_timed, out) and torch.equal(lse_timed, lse))
+
+    # Algorithmic work: valid entries (rows + index) and q per launch of the
+    # partial kernel; flops 2*512*H per entry for QK and again for PV.
+    n_valid = n_valid_slots
+    part_bytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * 512 * 2
+    step_bytes = part_bytes + B * H * (512 * 2 + 4)
+    flops = n_valid * 2048 * H
+    tokens_per_s = n_valid / (ms_per_step * 1e-3)
+    achieved = part_bytes / (kt_part * 1e-3) / 1e9
+    digest = _source_digest()
+    traffic = _traffic_from_profile(digest)
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "attended KV tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "long_lowbatch: B=1 H=64 topk=2048 swa=0, 131072 slots/seq, block 64, "
+                        "shuffled pages, 1% invalid, fp8_ds_mla rows, sink, sm_scale 512^-0.5",
+            "B": B, "H": H, "topk": w.topk, "swa": w.swa, "block_size": w.block_size,
+            "valid_entries": n_valid, "num_splits": S, "grid_partial": plan.grid_partial,
+            "replicas": R, "cache_pool_GB": round(R * nb * stride / 1e9, 2),
+            "graph_replay": True, "parallelism": "single GPU",
+        },
+        "achieved_hbm_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_partial_kernel<64>",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": part_bytes,
+            "mfma_frac": flops / (kt_part * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        },
+        "kernels_ms": {"convert": kt_conv, "decode_partial": kt_part, "combine": kt_comb},
+        "event_ms_per_step": ev_ms_per_step,
+        "cache_warm": {"ms_per_step": hot_ms_per_step, "decode_partial_ms": kt_part_hot,
+                       "tokens_per_s": n_valid / (hot_ms_per_step * 1e-3)},
+        "timed_output_matches_single_call": same,
+        "kernel_source_digest": digest,
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, out, lse, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def cpu_baseline(w, out_gpu, lse_gpu, seconds):
+    """The fp64 CPU oracle, as it stands, timed on this host over repeated
+    full decodes of the same workload (about `seconds` of CPU work)."""
+    import oracle
+    threads = oracle.default_threads()
+    reps, n_valid = 0, 0
+    t0 = time.perf_counter()
+    ref = None
+    while True:
+        ref_out, ref_lse, n_valid = oracle.decode_workload(w, nthreads=threads)
+        reps += 1
+        if ref is None:
+            ref = (ref_out, ref_lse)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    got = out_gpu.float().double().cpu().numpy()
+    err = np.abs(got - ref[0])
+    bound = 2e-2 + 1e-2 * np.abs(ref[0])
+    lse_err = float(np.max(np.abs(lse_gpu.double().cpu().numpy() - ref[1])))
+    return {
+        "value": reps * n_valid / dt,
+        "unit": "attended KV tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{reps} full decodes of the benchmark workload ({n_valid} valid entries x "
+                  f"64 heads each), fp64 C oracle, {threads} threads, {dt:.1f} s",
+        "host_cpus": os.cpu_count(),
+        "parity_vs_gpu": {"max_abs_out_err": float(err.max()),
+                          "within_tolerance": bool((err <= bound).all()) and lse_err <= 1e-3,
+                          "max_abs_lse_err": lse_err},
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -3,34 +3,39 @@
 //
 // Method sources (page titles):
 //   vLLM PR #52212, gfx950 DSV4 sparse decode page, implementation item 1:
-//     one 512-wide QK dot over 448 NoPE + 64 RoPE dims, PV in 4 slabs of 128
-//     dims, 32-row guarded tiles, masked tail, attention sink and invalid
-//     indices; item 2: split-K with per-row active splits.
+//     one 512-wide QK dot over 448 NoPE + 64 RoPE dims, 32-row guarded tiles,
+//     masked tail, attention sink and invalid indices; item 2: split-K with
+//     per-row active splits.
 //   SGLang PR #26208 report, key source snippets: fp8_ds_mla row and page
 //     layout, -1 invalid marker, top-k length mask; review highlights: a
 //     masked or -inf score contributes exactly zero to the running sum.
 //
-// One workgroup = 4 waves = 256 lanes serves one (token b, split s, head
-// group g).  Per tile of 32 cache rows:
-//   1. lanes 0..31 resolve their entry's page and byte offsets (int64);
-//   2. every lane gathers an 8-row x 8-dim patch (8-byte loads, coalesced in
-//      128-byte runs per row), dequantises FP8 x 2^(code-127) to bf16 and
-//      stores it twice in LDS: row-major (K operand of QK) and transposed
-//      (V operand of PV), so both MFMA operands are 16-byte LDS reads;
-//      rows that do not take part are stored as zeros, so no NaN in the
-//      cache can reach an MFMA;
-//   3. QK on bf16 MFMA 16x16x32 with q held in registers, scores scaled to
-//      base 2 and masked to -inf;
-//   4. online softmax (one head per 4 lanes, 8 scores each, butterfly
-//      reductions); the running sum takes the fp32 probabilities, the PV
-//      operand their bf16 rounding;
-//   5. PV on bf16 MFMA: wave w owns output dims [128w, 128w+128) for every
-//      head of the group (the 4 x 128 accumulator slabs), rescaled by the
-//      softmax correction before each tile.
-// With one split the epilogue folds the sink in and writes bf16 output and
-// lse; with several it writes the split's normalised fp32 partial and lse.
+// One workgroup = 8 waves serves one (token b, split s, head group g) and
+// walks its slice of the token's entry list in tiles of 32 cache rows.
+//   * Resolution (index -> page via the block table -> scale word) of 16
+//     tiles at a time, one entry per lane, into an LDS ring; the next half
+//     is resolved in four steps spread over two tile periods so its
+//     dependent loads overlap compute.
+//   * Waves 4..7 ("producers", 8 lanes per cache row) keep the raw bytes of
+//     the next two tiles in flight in registers, dequantise FP8 x 2^(code-127)
+//     to bf16 and store
+//     tile t+1 row-major into one half of a double-buffered LDS K tile while
+//   * waves 0..3 ("consumers", one per 16-head MFMA row tile) run QK of tile
+//     t on bf16 MFMA 16x16x32 (q held in registers) fused with the online
+//     softmax (DPP row reductions, lazy rescaling: the running max only moves
+//     when a score exceeds it by more than 2^8), writing bf16 probabilities;
+//   * then all 8 waves run PV on bf16 MFMA, wave w owning output dims
+//     [64w, 64w+64); the V operand comes straight from the row-major K tile
+//     through the gfx950 LDS transpose read, so no transposed copy is kept.
+// Rows that do not take part are stored as zeros, so a NaN in the cache can
+// never reach an MFMA.  The running sum takes the fp32 probabilities, the PV
+// operand their bf16 rounding.  With one split the epilogue folds the sink in
+// and writes bf16 output and lse; with several it writes the split's
+// normalised fp32 partial and lse.  Both leave through LDS as 16-byte stores.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "internal.hpp"
 
@@ -39,9 +44,15 @@ namespace dsv4 {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;   // log2 units a score may exceed the running max by
+constexpr int kStageLd = kD + 4;       // fp32 staging row (floats)
+constexpr int kStageLdBf = kD + 8;     // bf16 staging row (elements)
+constexpr int kHalfTiles = kMetaTiles / 2;
 
 // 2^(code-127) as an fp32 value: UE8M0 code 0 is the subnormal 2^-127 and
 // code 255 is NaN (the E8M0 encoding).
@@ -54,11 +65,12 @@ __device__ __forceinline__ float ue8m0_to_float(uint32_t code) {
 // decodes OCP E4M3FN exactly to fp32; the product is exact and so is its
 // bf16 rounding for every value a 4-bit-significand FP8 times 2^k can take
 // inside bf16's normal range.
-__device__ __forceinline__ void dequant8(uint2 raw, float scale, __bf16* v) {
+__device__ __forceinline__ bf16x8 dequant8(uint2 raw, float scale) {
     const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw.x, false);
     const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw.x, true);
     const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(raw.y, false);
     const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(raw.y, true);
+    bf16x8 v;
     v[0] = (__bf16)(a[0] * scale);
     v[1] = (__bf16)(a[1] * scale);
     v[2] = (__bf16)(b[0] * scale);
@@ -67,22 +79,127 @@ __device__ __forceinline__ void dequant8(uint2 raw, float scale, __bf16* v) {
     v[5] = (__bf16)(c[1] * scale);
     v[6] = (__bf16)(d[0] * scale);
     v[7] = (__bf16)(d[1] * scale);
+    return v;
+}
+
+// Reductions over the 16 lanes of a DPP row (lanes sharing lane >> 4):
+// quad xor 1, quad xor 2, half-row mirror, row mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    return fmaxf(v, dpp<0x140>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    return v + dpp<0x140>(v);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i%4 of the 4-element vectors addressed by lanes i/4 + 4k,
+// k = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// Producer lane pl (0..255) owns row pl/8 of a tile and, of the row's 72
+// eight-byte chunks (576 data bytes), chunks l8 + 8j for j = 0..8, l8 = pl%8:
+// j < 7 are NoPE chunks (8 FP8 dims scaled by code j of the row's scale
+// word), j = 7, 8 are RoPE chunks (4 bf16 dims each).  Every lane therefore
+// runs the same instructions; a wave reads 64 contiguous bytes from each of
+// 8 rows per load.  The raw chunks of a tile live in rr[O .. O+17].  The
+// loads are unconditional (a row that takes no part reads the pool's first
+// row and is zeroed when stored), so they issue back to back.
+// meta row: [doff (int64, -1 = the row takes no part), scale word (8 bytes)].
+constexpr int kChunks = 9;
+
+template <int O>
+__device__ __forceinline__ void load_patch(const DecodeParams& p, const int64_t* meta, int prow,
+                                           int l8, uint32_t (&rr)[64]) {
+    const int64_t d = max(meta[2 * prow], (int64_t)0);
+    const uint8_t* src = p.kv + d + 8 * l8;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src + 64 * j);
+        rr[O + 2 * j] = v.x;
+        rr[O + 2 * j + 1] = v.y;
+    }
+}
+
+// Dequantises the chunks into the row-major K tile.
+template <int O>
+__device__ __forceinline__ void store_patch(const uint32_t (&rr)[64], const int64_t* meta, int prow,
+                                            int l8, __bf16* Kn) {
+    const bool ok = meta[2 * prow] >= 0;
+    const uint64_t sw = ok ? (uint64_t)meta[2 * prow + 1] : 0x7F7F7F7F7F7F7F7Full;
+    __bf16* row = Kn + prow * kKnLd;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+        const uint2 raw = ok ? make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]) : make_uint2(0u, 0u);
+        const float sc = ue8m0_to_float((uint32_t)(sw >> (8 * j)) & 0xFFu);
+        *reinterpret_cast<bf16x8*>(row + 64 * j + 8 * l8) = dequant8(raw, sc);
+    }
+#pragma unroll
+    for (int j = 7; j < kChunks; ++j) {
+        const uint2 raw = ok ? make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]) : make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(row + kDNope + 32 * (j - 7) + 4 * l8) = raw;
+    }
+}
+
+// Entry resolution helpers: effective position -> index -> page -> scale word.
+__device__ __forceinline__ int32_t load_index(const DecodeParams& p, int b, int vl, int hi,
+                                              int pos) {
+    if (pos >= hi) return -1;
+    const int col = pos < vl ? pos : p.topk + (pos - vl);
+    return p.idx[(int64_t)b * p.idx_stride + col];
+}
+
+__device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, int b, int32_t idx) {
+    if (idx < 0) return -1;
+    const int64_t blk = idx / p.bs;
+    if (p.bt) {
+        if (blk >= p.max_blocks) return -1;
+        const int32_t pg = p.bt[(int64_t)b * p.bt_stride + blk];
+        return (pg >= 0 && pg < p.num_blocks) ? pg : -1;
+    }
+    return blk < p.num_blocks ? blk : -1;
+}
+
+__device__ __forceinline__ uint64_t load_scales(const DecodeParams& p, int64_t page, int32_t idx) {
+    if (page < 0) return 0;
+    const int64_t off = idx % p.bs;
+    return *reinterpret_cast<const uint64_t*>(p.kv + page * p.page_stride +
+                                              (int64_t)p.bs * kRowData + off * kRowScale);
+}
+
+__device__ __forceinline__ void write_meta(const DecodeParams& p, int64_t* row, int64_t page,
+                                           int32_t idx, uint64_t sw) {
+    row[0] = page >= 0 ? page * p.page_stride + (int64_t)(idx % p.bs) * kRowData : -1;
+    row[1] = (int64_t)sw;
 }
 
 template <int HG>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
-    constexpr int MT = HG / 16;              // 16-head MFMA row tiles
-    constexpr int TPW = (2 * MT + 3) / 4;    // QK output tiles per wave
+    constexpr int MT = HG / 16;              // 16-head MFMA row tiles; consumer wave w owns tile w
     static_assert(HG % 16 == 0 && HG <= kMaxHeadsPerGroup, "head group");
-
-    __shared__ __attribute__((aligned(16))) __bf16 Kn[kTile * kKnLd];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[kD * kVtLd];
-    __shared__ float Sb[HG * kSLd];
-    __shared__ __attribute__((aligned(16))) __bf16 Pb[HG * kPLd];
-    __shared__ __attribute__((aligned(16))) float alpha_s[HG];
-    __shared__ float fin_scale[HG];
-    __shared__ int64_t ent_doff[kTile];
-    __shared__ int64_t ent_soff[kTile];
+    using L = Smem<HG>;
+    static_assert(HG * kStageLdBf * 2 <= L::pb && 32 * kStageLd * 4 <= L::pb,
+                  "output staging must fit in the K tile region");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[L::bytes];
+    __bf16* Kn = reinterpret_cast<__bf16*>(smem + L::kn);          // [2][32][520]
+    __bf16* Pb = reinterpret_cast<__bf16*>(smem + L::pb);          // [HG][40]
+    float* alpha_s = reinterpret_cast<float*>(smem + L::alpha);
+    float* fin = reinterpret_cast<float*>(smem + L::fin);
+    int* flags = reinterpret_cast<int*>(smem + L::flags);
+    int64_t* meta = reinterpret_cast<int64_t*>(smem + L::meta);  // [32 tiles][32][2]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -91,9 +208,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // Work unit.  Workgroups are handed to the 8 XCDs round-robin; the head
     // groups of one (token, split) are kXcds apart so they land on the same
     // XCD and share its L2 for the rows they both read.
-    const int64_t L = blockIdx.x;
-    const int x = (int)(L % kXcds);
-    const int64_t r8 = L / kXcds;
+    const int64_t Lb = blockIdx.x;
+    const int x = (int)(Lb % kXcds);
+    const int64_t r8 = Lb / kXcds;
     const int g = (int)(r8 % p.G);
     const int64_t unit = (r8 / p.G) * kXcds + x;
     if (unit >= p.units) return;
@@ -109,264 +226,302 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     chunk = (chunk + kTile - 1) / kTile * kTile;
     const int lo = min(s * chunk, eff);
     const int hi = min(lo + chunk, eff);
+    const int ntiles = (hi - lo + kTile - 1) / kTile;
 
-    // q rows of this wave's 16-head QK tile stay in registers: A operand,
-    // lane (l16, lg) holds dims 32*ks + 8*lg .. +7 of head 16*mtq + l16.
-    const int qk_t0 = wave * TPW;
-    const bool has_qk = qk_t0 < 2 * MT;
-    const int mtq = has_qk ? qk_t0 / 2 : 0;
-    bf16x8 qa[16];
-    if (has_qk) {
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            p.q + ((int64_t)b * p.H + h0 + 16 * mtq + l16) * kD + 8 * lg);
+    const bool consumer = wave < MT;
+    const bool producer = wave >= 4;
+    const int ptid = tid - 4 * 64;
+    const int prow = ptid >> 3, l8 = ptid & 7;   // producer: tile row, chunk lane
+    auto meta_tile = [&](int t) { return meta + (t % kMetaTiles) * kTile * 2; };
+
+    // One 64-register array per lane, used by role: consumers keep the q
+    // rows of their 16 heads in it as the MFMA A operand (lane (l16, lg)
+    // holds dims 32*ks + 8*lg .. +7 of head 16*wave + l16 in rr[4ks..4ks+3]);
+    // producers keep two tiles of raw bytes in it (rr[0..31], rr[32..63]).
+    uint32_t rr[64];
+    if (consumer) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(
+            p.q + ((int64_t)b * p.H + h0 + 16 * wave + l16) * kD + 8 * lg);
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) qa[ks] = qp[4 * ks];
+        for (int ks = 0; ks < 16; ++ks) {
+            const u32x4 v = qp[4 * ks];
+            rr[4 * ks] = v[0];
+            rr[4 * ks + 1] = v[1];
+            rr[4 * ks + 2] = v[2];
+            rr[4 * ks + 3] = v[3];
+        }
     }
 
-    // Online-softmax state: head sh is owned by lanes 4*sh .. 4*sh+3, each
-    // keeping the same (m, l) in base-2 units.
-    const bool smx = tid < 4 * HG;
-    const int sh = tid >> 2, sp = tid & 3;
-    float m_run = -INFINITY, l_run = 0.f;
+    // Resolve tiles 0..15, one entry per lane.
+    {
+        const int32_t idx = load_index(p, b, vl, hi, lo + tid);
+        const int64_t pg = lookup_page(p, b, idx);
+        write_meta(p, meta + 2 * tid, pg, idx, load_scales(p, pg, idx));
+    }
+    __syncthreads();
 
-    f32x4 acc[MT][8];
+    if (producer) {
+        if (ntiles > 0) load_patch<0>(p, meta_tile(0), prow, l8, rr);
+        if (ntiles > 1) load_patch<32>(p, meta_tile(1), prow, l8, rr);
+        if (ntiles > 0) store_patch<0>(rr, meta_tile(0), prow, l8, Kn);
+        if (ntiles > 2) load_patch<0>(p, meta_tile(2), prow, l8, rr);
+    }
+    __syncthreads();
+
+    // Online-softmax state of a consumer's heads 16*wave + 4*lg + r
+    // (replicated over the 16 lanes of a DPP row), in base-2 units.
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m_run[r] = -INFINITY;
+        l_run[r] = 0.f;
+    }
+    f32x4 acc[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int t0 = lo; t0 < hi; t0 += kTile) {
-        // 1. Resolve entries.
-        if (tid < kTile) {
-            const int pos = t0 + tid;
-            int64_t doff = -1, soff = 0;
-            if (pos < hi) {
-                const int col = pos < vl ? pos : p.topk + (pos - vl);
-                const int32_t idx = p.idx[(int64_t)b * p.idx_stride + col];
-                if (idx >= 0) {
-                    const int64_t blk = idx / p.bs;
-                    const int64_t off = idx % p.bs;
-                    int64_t page = -1;
-                    if (p.bt) {
-                        if (blk < p.max_blocks) {
-                            const int32_t pg = p.bt[(int64_t)b * p.bt_stride + blk];
-                            if (pg >= 0 && pg < p.num_blocks) page = pg;
-                        }
-                    } else if (blk < p.num_blocks) {
-                        page = blk;
-                    }
-                    if (page >= 0) {
-                        doff = page * p.page_stride + off * kRowData;
-                        soff = page * p.page_stride + (int64_t)p.bs * kRowData + off * kRowScale;
-                    }
-                }
+    // Staged resolution of the next half (16 tiles), one entry per lane.
+    int32_t r_idx = -1;
+    int64_t r_pg = -1;
+    uint64_t r_sw = 0;
+
+    // One tile period; rr[O..O+31] holds tile t+1's raw bytes and receives
+    // tile t+3's (O = 32 for even t, 0 for odd t).
+    auto step = [&](int t, auto off) __attribute__((always_inline)) {
+        constexpr int O = decltype(off)::value;
+        const int ph = t % kHalfTiles;
+        const bool resolving = t - ph + kHalfTiles < ntiles;   // a next half exists
+        const int half_base = lo + (t - ph + kHalfTiles) * kTile;
+        // ---- B: QK + softmax (consumers) | dequant t+1, load t+3 (producers)
+        if (resolving && ph == 0) r_idx = load_index(p, b, vl, hi, half_base + tid);
+        if (resolving && ph == 1) r_sw = load_scales(p, r_pg, r_idx);
+        if (consumer) {
+            const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            const __bf16* k0 = &K[l16 * kKnLd + 8 * lg];
+            const __bf16* k1 = &K[(16 + l16) * kKnLd + 8 * lg];
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                const bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(k0 + 32 * ks);
+                const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(k1 + 32 * ks);
+                const bf16x8 qa = __builtin_bit_cast(
+                    bf16x8, u32x4{rr[4 * ks], rr[4 * ks + 1], rr[4 * ks + 2], rr[4 * ks + 3]});
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb0, s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb1, s1, 0, 0, 0);
             }
-            ent_doff[tid] = doff;
-            ent_soff[tid] = soff;
+            // lane holds S[head 16w + 4lg + r][row l16] (s0) and [row 16 + l16] (s1).
+            const int64_t* mt_t = meta_tile(t);
+            const bool ok0 = mt_t[2 * l16] >= 0;
+            const bool ok1 = mt_t[2 * (16 + l16)] >= 0;
+            f32x4 al;
+            bool moved = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x0 = ok0 ? s0[r] * p.qk_scale_log2 : -INFINITY;
+                const float x1 = ok1 ? s1[r] * p.qk_scale_log2 : -INFINITY;
+                const float mx = row_max16(fmaxf(x0, x1));
+                // Move the running max only when a score exceeds it by more
+                // than the slack (always on the first valid score).
+                const bool move = mx > m_run[r] + kRescaleSlack;
+                const float m_use = move ? mx : m_run[r];
+                float a = 1.f, e0 = 0.f, e1 = 0.f;
+                if (move) a = __builtin_amdgcn_exp2f(m_run[r] - mx);   // 0 when m_run = -inf
+                if (m_use != -INFINITY) {
+                    e0 = x0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x0 - m_use);
+                    e1 = x1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x1 - m_use);
+                }
+                l_run[r] = l_run[r] * a + row_sum16(e0 + e1);
+                m_run[r] = m_use;
+                al[r] = a;
+                moved |= move;
+                const int h = 16 * wave + 4 * lg + r;
+                Pb[h * kPLd + l16] = (__bf16)e0;
+                Pb[h * kPLd + 16 + l16] = (__bf16)e1;
+            }
+            if (l16 == 0) *reinterpret_cast<f32x4*>(&alpha_s[16 * wave + 4 * lg]) = al;
+            const bool any = __builtin_amdgcn_ballot_w64(moved) != 0;
+            if (lane == 0) flags[wave] = any ? 1 : 0;
+        }
+        if (producer) {
+            if (t + 1 < ntiles)
+                store_patch<O>(rr, meta_tile(t + 1), prow, l8, Kn + ((t + 1) & 1) * kTile * kKnLd);
+            if (t + 3 < ntiles) load_patch<O>(p, meta_tile(t + 3), prow, l8, rr);
         }
         __syncthreads();
 
-        // 2. Gather + dequantise an 8-row x 8-dim patch per lane.
+        // ---- C: PV (all waves) into output dims [64w, 64w+64).
+        if (resolving && ph == 0) r_pg = lookup_page(p, b, r_idx);
+        if (resolving && ph == 1)
+            write_meta(p, meta_tile(t - ph + kHalfTiles) + 2 * tid, r_pg, r_idx, r_sw);
         {
-            const int eg = tid & 3, dc = tid >> 2;   // rows 8eg..8eg+7, dims 8dc..8dc+7
-            __bf16 v[8][8];
-            if (dc < kDNope / 8) {
-                uint2 raw[8];
-                uint32_t code[8];
+            const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
+            bool rescale = false;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int64_t doff = ent_doff[8 * eg + i];
-                    raw[i] = make_uint2(0u, 0u);
-                    code[i] = 127u;
-                    if (doff >= 0) {
-                        raw[i] = *reinterpret_cast<const uint2*>(p.kv + doff + 8 * dc);
-                        code[i] = p.kv[ent_soff[8 * eg + i] + (dc >> 3)];
-                    }
-                }
+            for (int mt = 0; mt < MT; ++mt) rescale |= flags[mt] != 0;
+            bf16x8 pa[MT];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) dequant8(raw[i], ue8m0_to_float(code[i]), v[i]);
-            } else {
-                const int rd = dc - kDNope / 8;      // RoPE dims 448 + 8rd .. +7
+            for (int mt = 0; mt < MT; ++mt) {
+                pa[mt] = *reinterpret_cast<const bf16x8*>(&Pb[(16 * mt + l16) * kPLd + 8 * lg]);
+                if (rescale) {
+                    const f32x4 al = *reinterpret_cast<const f32x4*>(&alpha_s[16 * mt + 4 * lg]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int64_t doff = ent_doff[8 * eg + i];
-                    uint2 r0 = make_uint2(0u, 0u), r1 = make_uint2(0u, 0u);
-                    if (doff >= 0) {
-                        const uint8_t* src = p.kv + doff + kDNope + 16 * rd;
-                        r0 = *reinterpret_cast<const uint2*>(src);
-                        r1 = *reinterpret_cast<const uint2*>(src + 8);
-                    }
-                    const uint32_t w[4] = {r0.x, r0.y, r1.x, r1.y};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        v[i][2 * j] = __builtin_bit_cast(__bf16, (uint16_t)(w[j] & 0xFFFFu));
-                        v[i][2 * j + 1] = __builtin_bit_cast(__bf16, (uint16_t)(w[j] >> 16));
-                    }
+                    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] *= al;
                 }
             }
+            // V operand: lane j of 16-lane group lg points at rows 8lg + 4h + j/4,
+            // dims dimb + 4(j%4); the transpose read hands lane i dim dimb + i of
+            // rows 8lg + 4h .. +3.
+            const __bf16* vrow = &K[(8 * lg + (l16 >> 2)) * kKnLd + 64 * wave + 4 * (l16 & 3)];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                bf16x8 row;
+            for (int nt = 0; nt < 4; ++nt) {
+                const i16x4 v0 = lds_read_tr16(vrow + 16 * nt);
+                const i16x4 v1 = lds_read_tr16(vrow + 4 * kKnLd + 16 * nt);
+                const bf16x8 vb = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-                for (int j = 0; j < 8; ++j) row[j] = v[i][j];
-                *reinterpret_cast<bf16x8*>(&Kn[(8 * eg + i) * kKnLd + 8 * dc]) = row;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                bf16x8 col;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) col[i] = v[i][j];
-                *reinterpret_cast<bf16x8*>(&Vt[(8 * dc + j) * kVtLd + 8 * eg]) = col;
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, acc[mt][nt],
+                                                                          0, 0, 0);
             }
         }
         __syncthreads();
+    };
 
-        // 3. QK: S[head][row] = q . k in base-2 units, -inf where masked.
-        if (has_qk) {
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                const int tau = qk_t0 + j;
-                if (tau < 2 * MT) {
-                    const int nt = tau & 1;
-                    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-                    const __bf16* kp = &Kn[(16 * nt + l16) * kKnLd + 8 * lg];
-#pragma unroll
-                    for (int ks = 0; ks < 16; ++ks) {
-                        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kp + 32 * ks);
-                        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, sacc, 0, 0, 0);
-                    }
-                    const int n = 16 * nt + l16;
-                    const bool ok = ent_doff[n] >= 0;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        Sb[(16 * mtq + 4 * lg + r) * kSLd + n] =
-                            ok ? sacc[r] * p.qk_scale_log2 : -INFINITY;
-                }
-            }
-        }
-        __syncthreads();
-
-        // 4. Online softmax.
-        if (smx) {
-            float sv[8];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sv[i] = Sb[sh * kSLd + 8 * sp + i];
-                mx = fmaxf(mx, sv[i]);
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 1));
-            mx = fmaxf(mx, __shfl_xor(mx, 2));
-            const float m_new = fmaxf(m_run, mx);
-            float alpha = 1.f, psum = 0.f;
-            bf16x8 pv;
-            if (m_new == -INFINITY) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pv[i] = (__bf16)0.f;
-            } else {
-                alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float e = sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_new);
-                    pv[i] = (__bf16)e;
-                    psum += e;
-                }
-            }
-            psum += __shfl_xor(psum, 1);
-            psum += __shfl_xor(psum, 2);
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            *reinterpret_cast<bf16x8*>(&Pb[sh * kPLd + 8 * sp]) = pv;
-            if (sp == 0) alpha_s[sh] = alpha;
-        }
-        __syncthreads();
-
-        // 5. PV into the wave's 128-dim slab.
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 al = *reinterpret_cast<const f32x4*>(&alpha_s[16 * mt + 4 * lg]);
-            const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Pb[(16 * mt + l16) * kPLd + 8 * lg]);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 vb = *reinterpret_cast<const bf16x8*>(
-                    &Vt[(128 * wave + 16 * nt + l16) * kVtLd + 8 * lg]);
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[mt][nt] * al,
-                                                                      0, 0, 0);
-            }
-        }
-        __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, std::integral_constant<int, 32>{});
+        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 0>{});
     }
 
-    // Epilogue: per-head output scale and lse.
+    // Epilogue: per-head output scale and lse (lanes l16 == 0 of the consumers).
     const bool direct = p.S == 1;
-    if (smx && sp == 0) {
-        const int h = h0 + sh;
-        float scale, lse;
-        if (direct && p.sink) {
-            const float sk = p.sink[h] * kLog2e;
-            const float M = fmaxf(m_run, sk);
-            const float em = __builtin_amdgcn_exp2f(m_run - M);
-            const float D = l_run * em + __builtin_amdgcn_exp2f(sk - M);
-            scale = em / D;
-            lse = (M + __builtin_amdgcn_logf(D)) * kLn2;
-        } else if (l_run > 0.f) {
-            scale = 1.f / l_run;
-            lse = (m_run + __builtin_amdgcn_logf(l_run)) * kLn2;
-        } else {
-            scale = 0.f;
-            lse = -INFINITY;
-        }
-        fin_scale[sh] = scale;
-        if (direct) {
-            if (p.lse) p.lse[(int64_t)b * p.H + h] = lse;
-        } else {
-            p.part_lse[((int64_t)b * p.H + h) * p.S + s] = lse;
+    if (consumer && l16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int hl = 16 * wave + 4 * lg + r;
+            const int h = h0 + hl;
+            float scale, lse;
+            if (direct && p.sink) {
+                const float sk = p.sink[h] * kLog2e;
+                const float M = fmaxf(m_run[r], sk);
+                const float em = __builtin_amdgcn_exp2f(m_run[r] - M);
+                const float D = l_run[r] * em + __builtin_amdgcn_exp2f(sk - M);
+                scale = em / D;
+                lse = (M + __builtin_amdgcn_logf(D)) * kLn2;
+            } else if (l_run[r] > 0.f) {
+                scale = 1.f / l_run[r];
+                lse = (m_run[r] + __builtin_amdgcn_logf(l_run[r])) * kLn2;
+            } else {
+                scale = 0.f;
+                lse = -INFINITY;
+            }
+            fin[hl] = scale;
+            if (direct) {
+                if (p.lse) p.lse[(int64_t)b * p.H + h] = lse;
+            } else {
+                p.part_lse[((int64_t)b * p.H + h) * p.S + s] = lse;
+            }
         }
     }
     __syncthreads();
 
+    // Output through LDS: lane holds O[16mt + 4lg + r][64w + 16nt + l16].
+    if (direct) {
+        __bf16* st = reinterpret_cast<__bf16*>(smem);    // [HG][520]
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hl = 16 * mt + 4 * lg + r;
-            const float sc = fin_scale[hl];
-            const int64_t row = (int64_t)b * p.H + h0 + hl;
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const int d = 128 * wave + 16 * nt + l16;
-                const float val = acc[mt][nt][r] * sc;
-                if (direct)
-                    p.out[row * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)val);
-                else
-                    p.part_o[(row * p.S + s) * kD + d] = val;
+                for (int nt = 0; nt < 4; ++nt)
+                    st[(16 * mt + 4 * lg + r) * kStageLdBf + 64 * wave + 16 * nt + l16] =
+                        (__bf16)(acc[mt][nt][r] * sc[r]);
+        }
+        __syncthreads();
+        uint16_t* out = p.out + ((int64_t)b * p.H + h0) * kD;
+        for (int c = tid; c < HG * (kD / 8); c += kThreads) {
+            const int row = c >> 6, col = (c & 63) * 8;
+            *reinterpret_cast<bf16x8*>(out + (int64_t)row * kD + col) =
+                *reinterpret_cast<const bf16x8*>(&st[row * kStageLdBf + col]);
+        }
+    } else {
+        float* st = reinterpret_cast<float*>(smem);      // [32][516] per pass
+#pragma unroll
+        for (int pass = 0; pass < (MT + 1) / 2; ++pass) {
+            if (pass) __syncthreads();                   // previous pass fully read
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int mt = 2 * pass + m2;
+                if (mt < MT) {
+                    const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int nt = 0; nt < 4; ++nt)
+                            st[(16 * m2 + 4 * lg + r) * kStageLd + 64 * wave + 16 * nt + l16] =
+                                acc[mt][nt][r] * sc[r];
+                }
+            }
+            __syncthreads();
+            const int rows = min(32, HG - 32 * pass);
+            for (int c = tid; c < rows * (kD / 4); c += kThreads) {
+                const int row = c >> 7, col = (c & 127) * 4;
+                const int64_t bh = (int64_t)b * p.H + h0 + 32 * pass + row;
+                *reinterpret_cast<f32x4*>(p.part_o + (bh * p.S + s) * kD + col) =
+                    *reinterpret_cast<const f32x4*>(&st[row * kStageLd + col]);
             }
         }
     }
 }
 
 // Merge of split partials with the sink; one workgroup per (token, head),
-// 4 output dims per lane.
+// 4 output dims per lane.  The split lse values are uniform across the
+// workgroup; the partial loads of a chunk of splits are all issued before
+// any is used, and chunks are merged with an online rescale.
+constexpr int kCombineChunk = 16;
+
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % p.H);
     const float* ls = p.part_lse + bh * p.S;
-    const float sink = p.sink ? p.sink[h] : -INFINITY;
-    float M = sink;
-    for (int s = 0; s < p.S; ++s) M = fmaxf(M, ls[s]);
-    const int d = threadIdx.x * 4;
+    const float* po = p.part_o + bh * p.S * kD + threadIdx.x * 4;
+    float M = p.sink ? p.sink[h] : -INFINITY;
+    float D = p.sink ? 1.f : 0.f;                    // e^{sink - M} with M = sink
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < p.S; s0 += kCombineChunk) {
+        const int n = min(kCombineChunk, p.S - s0);
+        f32x4 v[kCombineChunk];
+        float l[kCombineChunk];
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j) {
+            if (j < n) {
+                l[j] = ls[s0 + j];
+                v[j] = *reinterpret_cast<const f32x4*>(po + (int64_t)(s0 + j) * kD);
+            }
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j)
+            if (j < n) cm = fmaxf(cm, l[j]);
+        const float M2 = fmaxf(M, cm);
+        if (M2 == -INFINITY) continue;               // nothing so far
+        const float c = __builtin_amdgcn_exp2f((M - M2) * kLog2e);   // 0 when M = -inf
+        D *= c;
+        o *= c;
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j) {
+            if (j < n && l[j] != -INFINITY) {
+                const float w = __builtin_amdgcn_exp2f((l[j] - M2) * kLog2e);
+                D += w;
+                o += w * v[j];
+            }
+        }
+        M = M2;
+    }
     float lse = -INFINITY;
     if (M != -INFINITY) {
-        float D = 0.f;
-        for (int s = 0; s < p.S; ++s) {
-            const float l = ls[s];
-            if (l == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f((l - M) * kLog2e);
-            D += w;
-            o += w * *reinterpret_cast<const f32x4*>(p.part_o + (bh * p.S + s) * kD + d);
-        }
-        if (p.sink) D += __builtin_amdgcn_exp2f((sink - M) * kLog2e);
         o *= 1.f / D;
         lse = M + __builtin_amdgcn_logf(D) * kLn2;
     }
@@ -375,7 +530,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[1]) << 16);
     packed.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[2]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[3]) << 16);
-    *reinterpret_cast<uint2*>(p.out + bh * kD + d) = packed;
+    *reinterpret_cast<uint2*>(p.out + bh * kD + threadIdx.x * 4) = packed;
     if (threadIdx.x == 0 && p.lse) p.lse[bh] = lse;
 }
 

@@ -17,9 +17,9 @@ constexpr int kRowData = 576;
 constexpr int kRowScale = 8;
 constexpr int kRowBytes = kRowData + kRowScale;
 
-// Decode kernel shape: 4 waves of 64 lanes, 32 cache rows per tile (the
+// Decode kernel shape: 8 waves of 64 lanes, 32 cache rows per tile (the
 // "BK32" tiles of the vLLM PR #52212 page), up to 64 heads per workgroup.
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kTile = 32;
 constexpr int kMaxHeadsPerGroup = 64;
 constexpr int kMaxSplits = 64;
@@ -27,16 +27,29 @@ constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin
 constexpr int kCombineThreads = 128;  // 4 output dims per thread
 
-// LDS tile geometry (bf16 elements unless noted); the +8 / +1 pads move
-// consecutive rows onto different banks.
-constexpr int kKnLd = kD + 8;       // row-major K tile  [32][520]
-constexpr int kVtLd = kTile + 8;    // transposed V tile [512][40]
-constexpr int kSLd = kTile + 1;     // scores, fp32      [HG][33]
-constexpr int kPLd = kTile + 8;     // probabilities    [HG][40]
+// LDS tile geometry.  The +8 pad moves consecutive rows onto different banks.
+constexpr int kKnLd = kD + 8;       // row-major K tile [32][520] bf16, double-buffered
+constexpr int kPLd = kTile + 8;     // probabilities    [HG][40] bf16
+constexpr int kMetaTiles = 32;      // resolved-entry ring: two halves of 16 tiles
+
+// LDS carve-up of the partial kernel (bytes).  The epilogue's staging area
+// reuses the K tile region once the last tile is done.
+template <int HG>
+struct Smem {
+    static constexpr int kn = 0;                                   // [2][32][520] bf16
+    static constexpr int pb = kn + 2 * kTile * kKnLd * 2;          // [HG][40] bf16
+    static constexpr int alpha = pb + HG * kPLd * 2;               // [HG] f32
+    static constexpr int fin = alpha + HG * 4;                     // [HG] f32
+    static constexpr int flags = fin + HG * 4;                     // [4] int
+    static constexpr int meta = flags + 16;                        // [32 tiles][32][2] int64
+    static constexpr int bytes = meta + kMetaTiles * kTile * 16;
+};
 
 constexpr size_t lds_bytes_for(int hg) {
-    return size_t(kTile) * kKnLd * 2 + size_t(kD) * kVtLd * 2 + size_t(hg) * kSLd * 4 +
-           size_t(hg) * kPLd * 2 + size_t(hg) * 4 * 2 + size_t(kTile) * 8 * 2;
+    return hg == 16 ? Smem<16>::bytes
+         : hg == 32 ? Smem<32>::bytes
+         : hg == 48 ? Smem<48>::bytes
+                    : Smem<64>::bytes;
 }
 
 struct DecodeParams {

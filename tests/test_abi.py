@@ -69,7 +69,7 @@ def test_plan_of_each_workload(ci):
     assert p.heads_per_group <= 64 and p.heads_per_group % 16 == 0
     units = c["B"] * S
     assert p.grid_partial == -(-units // 8) * 8 * p.head_groups
-    assert p.block_partial == 256
+    assert p.block_partial == 512
     if S > 1:
         assert p.workspace_bytes == c["B"] * c["H"] * S * 513 * 4
         assert p.grid_combine == c["B"] * c["H"]
