@@ -60,6 +60,12 @@ def _parse():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to defeat the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps one by one instead of replaying a graph "
+                         "(for hardware-counter runs, which count per dispatch)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before the steps, copy this many MB device-to-device once: a kernel "
+                         "of known traffic that calibrates the HBM byte counters")
     return ap.parse_args()
 
 
@@ -166,20 +172,41 @@ def main() -> int:
                 fn((offset + i) % R)
         return g
 
-    g_warm = capture(step, W) if W > 0 else None
-    g_main = capture(step, K, offset=W)
+    if args.calib_copy_mb:
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    # Warmup, then the timed region: exactly K steps.
-    if g_warm is not None:
-        g_warm.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    g_main.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.eager:
+        for i in range(W):
+            step(i % R)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for i in range(K):
+            step((W + i) % R)
+        ev1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        g_warm = capture(step, W) if W > 0 else None
+        g_main = capture(step, K, offset=W)
+        # Warmup, then the timed region: exactly K steps.
+        if g_warm is not None:
+            g_warm.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        g_main.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3
     ms_per_step = wall_ms / K
     ev_ms_per_step = ev0.elapsed_time(ev1) / K
@@ -244,7 +271,7 @@ def main() -> int:
             "B": B, "H": H, "topk": w.topk, "swa": w.swa, "block_size": w.block_size,
             "valid_entries": n_valid, "num_splits": S, "grid_partial": plan.grid_partial,
             "replicas": R, "cache_pool_GB": round(R * nb * stride / 1e9, 2),
-            "graph_replay": True, "parallelism": "single GPU",
+            "graph_replay": not args.eager, "parallelism": "single GPU",
         },
         "achieved_hbm_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {

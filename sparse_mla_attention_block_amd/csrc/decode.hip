@@ -12,10 +12,10 @@
 //
 // One workgroup = 8 waves serves one (token b, split s, head group g) and
 // walks its slice of the token's entry list in tiles of 32 cache rows.
-//   * Resolution (index -> page via the block table -> scale word) of 16
+//   * Resolution (index -> page via the block table -> byte offsets) of 16
 //     tiles at a time, one entry per lane, into an LDS ring; the next half
-//     is resolved in four steps spread over two tile periods so its
-//     dependent loads overlap compute.
+//     is resolved in steps spread over two tile periods so its dependent
+//     loads overlap compute.
 //   * Waves 4..7 ("producers", 8 lanes per cache row) keep the raw bytes of
 //     the next two tiles in flight in registers, dequantise FP8 x 2^(code-127)
 //     to bf16 and store
@@ -50,8 +50,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;   // log2 units a score may exceed the running max by
-constexpr int kStageLd = kD + 4;       // fp32 staging row (floats)
-constexpr int kStageLdBf = kD + 8;     // bf16 staging row (elements)
 constexpr int kHalfTiles = kMetaTiles / 2;
 
 // 2^(code-127) as an fp32 value: UE8M0 code 0 is the subnormal 2^-127 and
@@ -115,10 +113,12 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const __bf16* p) {
 // j < 7 are NoPE chunks (8 FP8 dims scaled by code j of the row's scale
 // word), j = 7, 8 are RoPE chunks (4 bf16 dims each).  Every lane therefore
 // runs the same instructions; a wave reads 64 contiguous bytes from each of
-// 8 rows per load.  The raw chunks of a tile live in rr[O .. O+17].  The
-// loads are unconditional (a row that takes no part reads the pool's first
-// row and is zeroed when stored), so they issue back to back.
-// meta row: [doff (int64, -1 = the row takes no part), scale word (8 bytes)].
+// 8 rows per load.  The raw chunks of a tile live in rr[O .. O+17] and the
+// row's scale word in rr[O+18 .. O+19].  The loads are unconditional (a row
+// that takes no part reads the pool's first row and is zeroed when stored),
+// so they issue back to back.
+// meta row: [byte offset of the row's data (-1 = the row takes no part),
+//            byte offset of its scale word].
 constexpr int kChunks = 9;
 
 template <int O>
@@ -126,12 +126,15 @@ __device__ __forceinline__ void load_patch(const DecodeParams& p, const int64_t*
                                            int l8, uint32_t (&rr)[64]) {
     const int64_t d = max(meta[2 * prow], (int64_t)0);
     const uint8_t* src = p.kv + d + 8 * l8;
+    const uint2 sw = *reinterpret_cast<const uint2*>(p.kv + meta[2 * prow + 1]);
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
         const uint2 v = *reinterpret_cast<const uint2*>(src + 64 * j);
         rr[O + 2 * j] = v.x;
         rr[O + 2 * j + 1] = v.y;
     }
+    rr[O + 18] = sw.x;
+    rr[O + 19] = sw.y;
 }
 
 // Dequantises the chunks into the row-major K tile.
@@ -139,7 +142,7 @@ template <int O>
 __device__ __forceinline__ void store_patch(const uint32_t (&rr)[64], const int64_t* meta, int prow,
                                             int l8, __bf16* Kn) {
     const bool ok = meta[2 * prow] >= 0;
-    const uint64_t sw = ok ? (uint64_t)meta[2 * prow + 1] : 0x7F7F7F7F7F7F7F7Full;
+    const uint64_t sw = ok ? ((uint64_t)rr[O + 19] << 32 | rr[O + 18]) : 0x7F7F7F7F7F7F7F7Full;
     __bf16* row = Kn + prow * kKnLd;
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
@@ -173,17 +176,14 @@ __device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, int b, int
     return blk < p.num_blocks ? blk : -1;
 }
 
-__device__ __forceinline__ uint64_t load_scales(const DecodeParams& p, int64_t page, int32_t idx) {
-    if (page < 0) return 0;
-    const int64_t off = idx % p.bs;
-    return *reinterpret_cast<const uint64_t*>(p.kv + page * p.page_stride +
-                                              (int64_t)p.bs * kRowData + off * kRowScale);
-}
-
+// Data and scale-word byte offsets of the row at (page, idx % bs); a row that
+// takes no part gets data offset -1 and scale offset 0 (the pool's first
+// bytes, read and discarded).
 __device__ __forceinline__ void write_meta(const DecodeParams& p, int64_t* row, int64_t page,
-                                           int32_t idx, uint64_t sw) {
-    row[0] = page >= 0 ? page * p.page_stride + (int64_t)(idx % p.bs) * kRowData : -1;
-    row[1] = (int64_t)sw;
+                                           int32_t idx) {
+    const int64_t off = idx % p.bs;
+    row[0] = page >= 0 ? page * p.page_stride + off * kRowData : -1;
+    row[1] = page >= 0 ? page * p.page_stride + (int64_t)p.bs * kRowData + off * kRowScale : 0;
 }
 
 template <int HG>
@@ -191,8 +191,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     constexpr int MT = HG / 16;              // 16-head MFMA row tiles; consumer wave w owns tile w
     static_assert(HG % 16 == 0 && HG <= kMaxHeadsPerGroup, "head group");
     using L = Smem<HG>;
-    static_assert(HG * kStageLdBf * 2 <= L::pb && 32 * kStageLd * 4 <= L::pb,
-                  "output staging must fit in the K tile region");
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::bytes];
     __bf16* Kn = reinterpret_cast<__bf16*>(smem + L::kn);          // [2][32][520]
     __bf16* Pb = reinterpret_cast<__bf16*>(smem + L::pb);          // [HG][40]
@@ -256,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     {
         const int32_t idx = load_index(p, b, vl, hi, lo + tid);
         const int64_t pg = lookup_page(p, b, idx);
-        write_meta(p, meta + 2 * tid, pg, idx, load_scales(p, pg, idx));
+        write_meta(p, meta + 2 * tid, pg, idx);
     }
     __syncthreads();
 
@@ -285,7 +283,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // Staged resolution of the next half (16 tiles), one entry per lane.
     int32_t r_idx = -1;
     int64_t r_pg = -1;
-    uint64_t r_sw = 0;
 
     // One tile period; rr[O..O+31] holds tile t+1's raw bytes and receives
     // tile t+3's (O = 32 for even t, 0 for odd t).
@@ -296,7 +293,6 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         const int half_base = lo + (t - ph + kHalfTiles) * kTile;
         // ---- B: QK + softmax (consumers) | dequant t+1, load t+3 (producers)
         if (resolving && ph == 0) r_idx = load_index(p, b, vl, hi, half_base + tid);
-        if (resolving && ph == 1) r_sw = load_scales(p, r_pg, r_idx);
         if (consumer) {
             const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
             f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -354,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         // ---- C: PV (all waves) into output dims [64w, 64w+64).
         if (resolving && ph == 0) r_pg = lookup_page(p, b, r_idx);
         if (resolving && ph == 1)
-            write_meta(p, meta_tile(t - ph + kHalfTiles) + 2 * tid, r_pg, r_idx, r_sw);
+            write_meta(p, meta_tile(t - ph + kHalfTiles) + 2 * tid, r_pg, r_idx);
         {
             const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
             bool rescale = false;
@@ -428,7 +424,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
     // Output through LDS: lane holds O[16mt + 4lg + r][64w + 16nt + l16].
     if (direct) {
-        __bf16* st = reinterpret_cast<__bf16*>(smem);    // [HG][520]
+        constexpr int LD = L::stage_ld_bf16;
+        __bf16* st = reinterpret_cast<__bf16*>(smem + L::stage);    // [HG][520]
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
@@ -436,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
-                    st[(16 * mt + 4 * lg + r) * kStageLdBf + 64 * wave + 16 * nt + l16] =
+                    st[(16 * mt + 4 * lg + r) * LD + 64 * wave + 16 * nt + l16] =
                         (__bf16)(acc[mt][nt][r] * sc[r]);
         }
         __syncthreads();
@@ -444,44 +441,37 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         for (int c = tid; c < HG * (kD / 8); c += kThreads) {
             const int row = c >> 6, col = (c & 63) * 8;
             *reinterpret_cast<bf16x8*>(out + (int64_t)row * kD + col) =
-                *reinterpret_cast<const bf16x8*>(&st[row * kStageLdBf + col]);
+                *reinterpret_cast<const bf16x8*>(&st[row * LD + col]);
         }
     } else {
-        float* st = reinterpret_cast<float*>(smem);      // [32][516] per pass
+        constexpr int LD = L::stage_ld_f32;
+        float* st = reinterpret_cast<float*>(smem + L::stage);      // [HG][516]
 #pragma unroll
-        for (int pass = 0; pass < (MT + 1) / 2; ++pass) {
-            if (pass) __syncthreads();                   // previous pass fully read
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
 #pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2) {
-                const int mt = 2 * pass + m2;
-                if (mt < MT) {
-                    const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-#pragma unroll
-                        for (int nt = 0; nt < 4; ++nt)
-                            st[(16 * m2 + 4 * lg + r) * kStageLd + 64 * wave + 16 * nt + l16] =
-                                acc[mt][nt][r] * sc[r];
-                }
-            }
-            __syncthreads();
-            const int rows = min(32, HG - 32 * pass);
-            for (int c = tid; c < rows * (kD / 4); c += kThreads) {
-                const int row = c >> 7, col = (c & 127) * 4;
-                const int64_t bh = (int64_t)b * p.H + h0 + 32 * pass + row;
-                *reinterpret_cast<f32x4*>(p.part_o + (bh * p.S + s) * kD + col) =
-                    *reinterpret_cast<const f32x4*>(&st[row * kStageLd + col]);
-            }
+                for (int nt = 0; nt < 4; ++nt)
+                    st[(16 * mt + 4 * lg + r) * LD + 64 * wave + 16 * nt + l16] =
+                        acc[mt][nt][r] * sc[r];
+        }
+        __syncthreads();
+        for (int c = tid; c < HG * (kD / 4); c += kThreads) {
+            const int row = c >> 7, col = (c & 127) * 4;
+            const int64_t bh = (int64_t)b * p.H + h0 + row;
+            *reinterpret_cast<f32x4*>(p.part_o + (bh * p.S + s) * kD + col) =
+                *reinterpret_cast<const f32x4*>(&st[row * LD + col]);
         }
     }
 }
 
 // Merge of split partials with the sink; one workgroup per (token, head),
-// 4 output dims per lane.  The split lse values are uniform across the
-// workgroup; the partial loads of a chunk of splits are all issued before
-// any is used, and chunks are merged with an online rescale.
-constexpr int kCombineChunk = 16;
-
+// 4 output dims per lane.  Splits are taken NB at a time (NB = the split
+// count rounded up to a power of two, at most 32): every partial and lse load
+// of a batch is issued before any is used (one memory round trip per batch),
+// and batches are merged with an online rescale.
+template <int kCombineBatch>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineParams p) {
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % p.H);
@@ -490,33 +480,29 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     float M = p.sink ? p.sink[h] : -INFINITY;
     float D = p.sink ? 1.f : 0.f;                    // e^{sink - M} with M = sink
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < p.S; s0 += kCombineChunk) {
-        const int n = min(kCombineChunk, p.S - s0);
-        f32x4 v[kCombineChunk];
-        float l[kCombineChunk];
+    for (int s0 = 0; s0 < p.S; s0 += kCombineBatch) {
+        const int n = min(kCombineBatch, p.S - s0);
+        f32x4 v[kCombineBatch];
+        float l[kCombineBatch];
 #pragma unroll
-        for (int j = 0; j < kCombineChunk; ++j) {
-            if (j < n) {
-                l[j] = ls[s0 + j];
-                v[j] = *reinterpret_cast<const f32x4*>(po + (int64_t)(s0 + j) * kD);
-            }
+        for (int j = 0; j < kCombineBatch; ++j) {
+            l[j] = j < n ? ls[s0 + j] : -INFINITY;
+            v[j] = j < n ? *reinterpret_cast<const f32x4*>(po + (int64_t)(s0 + j) * kD)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         float cm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kCombineChunk; ++j)
-            if (j < n) cm = fmaxf(cm, l[j]);
+        for (int j = 0; j < kCombineBatch; ++j) cm = fmaxf(cm, l[j]);
         const float M2 = fmaxf(M, cm);
         if (M2 == -INFINITY) continue;               // nothing so far
         const float c = __builtin_amdgcn_exp2f((M - M2) * kLog2e);   // 0 when M = -inf
         D *= c;
         o *= c;
 #pragma unroll
-        for (int j = 0; j < kCombineChunk; ++j) {
-            if (j < n && l[j] != -INFINITY) {
-                const float w = __builtin_amdgcn_exp2f((l[j] - M2) * kLog2e);
-                D += w;
-                o += w * v[j];
-            }
+        for (int j = 0; j < kCombineBatch; ++j) {
+            const float w = l[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((l[j] - M2) * kLog2e);
+            D += w;
+            o += w * v[j];
         }
         M = M2;
     }
@@ -548,8 +534,15 @@ hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.B * p.H;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(kCombineThreads), 0, stream, p);
+    const dim3 g((unsigned)((int64_t)p.B * p.H)), blk(kCombineThreads);
+    if (p.S <= 4)
+        hipLaunchKernelGGL(combine_kernel<4>, g, blk, 0, stream, p);
+    else if (p.S <= 8)
+        hipLaunchKernelGGL(combine_kernel<8>, g, blk, 0, stream, p);
+    else if (p.S <= 16)
+        hipLaunchKernelGGL(combine_kernel<16>, g, blk, 0, stream, p);
+    else
+        hipLaunchKernelGGL(combine_kernel<32>, g, blk, 0, stream, p);
     return hipGetLastError();
 }
 
