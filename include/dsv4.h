@@ -164,8 +164,9 @@ int dsv4_sparse_decode(const dsv4_decode_desc* desc, const void* q, const void* 
  * directly (the same bytes dsv4_sparse_decode writes).  With S > 1 it
  * writes, for every (b, h, split), the split's normalised partial output
  * and its log-sum-exp without the sink, into the workspace:
- *   part_out = (float*)workspace            [B, H, S, 512]
- *   part_lse = part_out + B*H*S*512         [B, H, S]
+ *   part_out = (bf16*)workspace                       bf16 [B, H, S, 512] (RNE)
+ *   part_lse = (float*)(part_out + B*H*S*512)         float [B, H, S]
+ * (B*H*S*1028 bytes in all).
  * A split with no taking-part entry writes 0 and -inf.  Splits cover the
  * row's effective list main[0:valid_len] ++ swa in contiguous chunks
  * (vLLM PR #52212 page, implementation item 2: per-row active splits under
@@ -184,11 +185,11 @@ int dsv4_sparse_decode_partial(const dsv4_decode_desc* desc, const void* q,
  * All splits empty: out = 0, lse = sink[h] (or -inf without a sink).
  * (SGLang PR #26208 report, implementation item 3: split-K over the top-k
  * axis; vLLM PR #52212 page: the reduce of split partials.)
- *   part_out float [B, H, S, 512], part_lse float [B, H, S] (16-byte aligned),
+ *   part_out bf16 [B, H, S, 512] (8-byte aligned), part_lse float [B, H, S],
  *   sink float [H] or NULL, out bf16 [B, H, 512], lse float [B, H] or NULL.
  * Also serves partials computed elsewhere (e.g. on other GPUs). */
 int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
-                        const float* part_out, const float* part_lse, const float* sink,
+                        const void* part_out, const float* part_lse, const float* sink,
                         void* out, float* lse, hipStream_t stream);
 
 /* ------------------------------------------------- index conversion */

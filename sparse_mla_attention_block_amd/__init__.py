@@ -193,9 +193,10 @@ def dsv4_convert_req_index_to_global(req_id: Optional[torch.Tensor], num_reqs: i
 
 def workspace_split_views(workspace: torch.Tensor, batch: int, num_heads: int,
                           num_splits: int):
-    """(part_out [B,H,S,512], part_lse [B,H,S]) views of a decode workspace,
-    as laid out by dsv4_sparse_decode_partial."""
+    """(part_out bf16 [B,H,S,512], part_lse float32 [B,H,S]) views of a decode
+    workspace (a flat uint8 tensor), as laid out by dsv4_sparse_decode_partial."""
     n = batch * num_heads * num_splits
-    f = workspace.view(torch.float32)
-    return f[: n * 512].view(batch, num_heads, num_splits, 512), \
-        f[n * 512: n * 513].view(batch, num_heads, num_splits)
+    w = workspace.view(torch.uint8)
+    part_out = w[: n * 1024].view(torch.bfloat16).view(batch, num_heads, num_splits, 512)
+    part_lse = w[n * 1024: n * 1028].view(torch.float32).view(batch, num_heads, num_splits)
+    return part_out, part_lse

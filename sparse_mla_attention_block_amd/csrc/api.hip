@@ -119,7 +119,8 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         plan->grid_combine = S > 1 ? (int64_t)d->batch * d->num_heads : 0;
         plan->block_combine = S > 1 ? kCombineThreads : 0;
         plan->workspace_bytes =
-            S > 1 ? (size_t)d->batch * d->num_heads * S * (kD + 1) * sizeof(float) : 0;
+            S > 1 ? (size_t)d->batch * d->num_heads * S * (kD * sizeof(uint16_t) + sizeof(float))
+                  : 0;
         plan->lds_bytes = lds_bytes_for(hg);
     }
     return DSV4_OK;
@@ -166,8 +167,10 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
     const size_t n_part = (size_t)d->batch * d->num_heads * sh.splits * dsv4::kD;
-    p.part_o = sh.splits > 1 ? static_cast<float*>(d->workspace) : nullptr;
-    p.part_lse = sh.splits > 1 ? static_cast<float*>(d->workspace) + n_part : nullptr;
+    p.part_o = sh.splits > 1 ? static_cast<uint16_t*>(d->workspace) : nullptr;
+    p.part_lse = sh.splits > 1
+                     ? reinterpret_cast<float*>(static_cast<uint16_t*>(d->workspace) + n_part)
+                     : nullptr;
     p.num_blocks = d->num_blocks;
     p.bt_stride = d->block_table_stride;
     p.page_stride = d->page_stride;
@@ -266,7 +269,7 @@ int dsv4_sparse_decode_partial(const dsv4_decode_desc* desc, const void* q,
 }
 
 int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
-                        const float* part_out, const float* part_lse, const float* sink,
+                        const void* part_out, const float* part_lse, const float* sink,
                         void* out, float* lse, hipStream_t stream) {
     if (batch < 1 || num_heads < 1 || num_splits < 1)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "batch, num_heads and num_splits must be >= 1");
@@ -274,11 +277,11 @@ int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
         return fail(DSV4_ERR_INVALID_ARGUMENT, "batch * num_heads too large");
     if (!part_out || !part_lse || !out)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "part_out, part_lse and out must not be NULL");
-    if (!aligned(part_out, 16) || !aligned(out, 8) || !aligned(part_lse, 4))
+    if (!aligned(part_out, 8) || !aligned(out, 8) || !aligned(part_lse, 4))
         return fail(DSV4_ERR_INVALID_ARGUMENT,
-                    "part_out must be 16-byte aligned, out 8-byte aligned");
+                    "part_out and out must be 8-byte aligned, part_lse 4-byte aligned");
     dsv4::CombineParams c;
-    c.part_o = part_out;
+    c.part_o = static_cast<const uint16_t*>(part_out);
     c.part_lse = part_lse;
     c.sink = sink;
     c.out = static_cast<uint16_t*>(out);

@@ -186,9 +186,32 @@ __device__ __forceinline__ void write_meta(const DecodeParams& p, int64_t* row, 
     row[1] = page >= 0 ? page * p.page_stride + (int64_t)p.bs * kRowData + off * kRowScale : 0;
 }
 
+// Reductions across the four 16-lane rows of a wave.  v_permlane16_swap
+// exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second, v_permlane32_swap the upper 32 lanes of the first with the
+// lower 32 of the second; with both operands holding v, every lane ends up
+// with the two values of its row pair (half pair).  Written as inline asm:
+// the optimiser of this compiler folds the builtins' second result into the
+// first.  The s_nop covers the VALU-write to permlane-read hazard.
+template <class Op>
+__device__ __forceinline__ float xrow4(float v, Op op) {
+    uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+    x = __builtin_bit_cast(uint32_t, op(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y)));
+    y = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+    return op(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+}
+__device__ __forceinline__ float xrow_max4(float v) {
+    return xrow4(v, [](float p, float q) { return fmaxf(p, q); });
+}
+__device__ __forceinline__ float xrow_sum4(float v) {
+    return xrow4(v, [](float p, float q) { return p + q; });
+}
+
 template <int HG>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
-    constexpr int MT = HG / 16;              // 16-head MFMA row tiles; consumer wave w owns tile w
+    constexpr int MT = HG / 16;              // 16-head MFMA tiles; consumer wave w owns tile w
     static_assert(HG % 16 == 0 && HG <= kMaxHeadsPerGroup, "head group");
     using L = Smem<HG>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::bytes];
@@ -197,7 +220,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     float* alpha_s = reinterpret_cast<float*>(smem + L::alpha);
     float* fin = reinterpret_cast<float*>(smem + L::fin);
     int* flags = reinterpret_cast<int*>(smem + L::flags);
-    int64_t* meta = reinterpret_cast<int64_t*>(smem + L::meta);  // [32 tiles][32][2]
+    uint32_t* vmask = reinterpret_cast<uint32_t*>(smem + L::vmask);  // [32 tiles]
+    int64_t* meta = reinterpret_cast<int64_t*>(smem + L::meta);    // [32 tiles][32][2]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -230,16 +254,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     const bool producer = wave >= 4;
     const int ptid = tid - 4 * 64;
     const int prow = ptid >> 3, l8 = ptid & 7;   // producer: tile row, chunk lane
+    const int hc = 16 * wave + l16;              // consumer lane's head (within the group)
     auto meta_tile = [&](int t) { return meta + (t % kMetaTiles) * kTile * 2; };
 
     // One 64-register array per lane, used by role: consumers keep the q
-    // rows of their 16 heads in it as the MFMA A operand (lane (l16, lg)
-    // holds dims 32*ks + 8*lg .. +7 of head 16*wave + l16 in rr[4ks..4ks+3]);
-    // producers keep two tiles of raw bytes in it (rr[0..31], rr[32..63]).
+    // row of their head in it (lane (l16, lg) holds dims 32*ks + 8*lg .. +7
+    // of head 16*wave + l16 in rr[4ks..4ks+3], the B operand of QK);
+    // producers keep two tiles of raw bytes in it (rr[0..19], rr[32..51]).
     uint32_t rr[64];
+    float sink_l2 = -INFINITY;                   // consumer lane's sink, base-2 units
     if (consumer) {
         const u32x4* qp = reinterpret_cast<const u32x4*>(
-            p.q + ((int64_t)b * p.H + h0 + 16 * wave + l16) * kD + 8 * lg);
+            p.q + ((int64_t)b * p.H + h0 + hc) * kD + 8 * lg);
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
             const u32x4 v = qp[4 * ks];
@@ -248,13 +274,22 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             rr[4 * ks + 2] = v[2];
             rr[4 * ks + 3] = v[3];
         }
+        if (p.sink) sink_l2 = p.sink[h0 + hc] * kLog2e;
     }
 
-    // Resolve tiles 0..15, one entry per lane.
+    // Resolution of 16 tiles: one entry per lane, then a per-tile bit mask of
+    // the rows that take part (each wave covers two tiles).
+    auto publish = [&](int first_tile, int64_t page, int32_t idx) {
+        write_meta(p, meta_tile(first_tile) + 2 * tid, page, idx);
+        const uint64_t bits = __builtin_amdgcn_ballot_w64(page >= 0);
+        if (lane == 0) {
+            vmask[(first_tile + 2 * wave) % kMetaTiles] = (uint32_t)bits;
+            vmask[(first_tile + 2 * wave + 1) % kMetaTiles] = (uint32_t)(bits >> 32);
+        }
+    };
     {
         const int32_t idx = load_index(p, b, vl, hi, lo + tid);
-        const int64_t pg = lookup_page(p, b, idx);
-        write_meta(p, meta + 2 * tid, pg, idx);
+        publish(0, lookup_page(p, b, idx), idx);
     }
     __syncthreads();
 
@@ -266,14 +301,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     }
     __syncthreads();
 
-    // Online-softmax state of a consumer's heads 16*wave + 4*lg + r
-    // (replicated over the 16 lanes of a DPP row), in base-2 units.
-    float m_run[4], l_run[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m_run[r] = -INFINITY;
-        l_run[r] = 0.f;
-    }
+    // Online-softmax state of a consumer lane's head, in base-2 units
+    // (replicated over the lane's four 16-lane rows).
+    float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -284,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     int32_t r_idx = -1;
     int64_t r_pg = -1;
 
-    // One tile period; rr[O..O+31] holds tile t+1's raw bytes and receives
+    // One tile period; rr[O..O+19] holds tile t+1's raw bytes and receives
     // tile t+3's (O = 32 for even t, 0 for odd t).
     auto step = [&](int t, auto off) __attribute__((always_inline)) {
         constexpr int O = decltype(off)::value;
@@ -294,6 +324,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         // ---- B: QK + softmax (consumers) | dequant t+1, load t+3 (producers)
         if (resolving && ph == 0) r_idx = load_index(p, b, vl, hi, half_base + tid);
         if (consumer) {
+            // S^T = K q^T: A operand = K rows (entries), B operand = q (heads).
             const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
             f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
             const __bf16* k0 = &K[l16 * kKnLd + 8 * lg];
@@ -302,42 +333,45 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             for (int ks = 0; ks < 16; ++ks) {
                 const bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(k0 + 32 * ks);
                 const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(k1 + 32 * ks);
-                const bf16x8 qa = __builtin_bit_cast(
+                const bf16x8 qb = __builtin_bit_cast(
                     bf16x8, u32x4{rr[4 * ks], rr[4 * ks + 1], rr[4 * ks + 2], rr[4 * ks + 3]});
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb0, s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kb1, s1, 0, 0, 0);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb0, qb, s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb1, qb, s1, 0, 0, 0);
             }
-            // lane holds S[head 16w + 4lg + r][row l16] (s0) and [row 16 + l16] (s1).
-            const int64_t* mt_t = meta_tile(t);
-            const bool ok0 = mt_t[2 * l16] >= 0;
-            const bool ok1 = mt_t[2 * (16 + l16)] >= 0;
-            f32x4 al;
-            bool moved = false;
+            // lane holds the scores of head hc for rows 4lg + r (s0) and 16 + 4lg + r (s1).
+            const uint32_t vm = vmask[t % kMetaTiles];
+            float x[8];
+            float mx = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float x0 = ok0 ? s0[r] * p.qk_scale_log2 : -INFINITY;
-                const float x1 = ok1 ? s1[r] * p.qk_scale_log2 : -INFINITY;
-                const float mx = row_max16(fmaxf(x0, x1));
-                // Move the running max only when a score exceeds it by more
-                // than the slack (always on the first valid score).
-                const bool move = mx > m_run[r] + kRescaleSlack;
-                const float m_use = move ? mx : m_run[r];
-                float a = 1.f, e0 = 0.f, e1 = 0.f;
-                if (move) a = __builtin_amdgcn_exp2f(m_run[r] - mx);   // 0 when m_run = -inf
-                if (m_use != -INFINITY) {
-                    e0 = x0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x0 - m_use);
-                    e1 = x1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x1 - m_use);
-                }
-                l_run[r] = l_run[r] * a + row_sum16(e0 + e1);
-                m_run[r] = m_use;
-                al[r] = a;
-                moved |= move;
-                const int h = 16 * wave + 4 * lg + r;
-                Pb[h * kPLd + l16] = (__bf16)e0;
-                Pb[h * kPLd + 16 + l16] = (__bf16)e1;
+                x[r] = (vm >> (4 * lg + r)) & 1u ? s0[r] * p.qk_scale_log2 : -INFINITY;
+                x[4 + r] = (vm >> (16 + 4 * lg + r)) & 1u ? s1[r] * p.qk_scale_log2 : -INFINITY;
+                mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
             }
-            if (l16 == 0) *reinterpret_cast<f32x4*>(&alpha_s[16 * wave + 4 * lg]) = al;
-            const bool any = __builtin_amdgcn_ballot_w64(moved) != 0;
+            mx = xrow_max4(mx);
+            // Move the running max only when a score exceeds it by more than
+            // the slack (always on the first valid score).
+            const bool move = mx > m_run + kRescaleSlack;
+            const float m_use = move ? mx : m_run;
+            const float a = move ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;   // 0 if m_run = -inf
+            float e[8], psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                e[i] = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_use);
+                psum += e[i];
+            }
+            l_run = l_run * a + xrow_sum4(psum);
+            m_run = m_use;
+            bf16x8 pv;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = (__bf16)e[i];
+            __bf16* prow_p = Pb + hc * kPLd + 4 * lg;
+            *reinterpret_cast<uint2*>(prow_p) = __builtin_bit_cast(
+                uint2, __builtin_shufflevector(pv, pv, 0, 1, 2, 3));
+            *reinterpret_cast<uint2*>(prow_p + 16) = __builtin_bit_cast(
+                uint2, __builtin_shufflevector(pv, pv, 4, 5, 6, 7));
+            if (lg == 0) alpha_s[hc] = a;
+            const bool any = __builtin_amdgcn_ballot_w64(move) != 0;
             if (lane == 0) flags[wave] = any ? 1 : 0;
         }
         if (producer) {
@@ -349,8 +383,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
         // ---- C: PV (all waves) into output dims [64w, 64w+64).
         if (resolving && ph == 0) r_pg = lookup_page(p, b, r_idx);
-        if (resolving && ph == 1)
-            write_meta(p, meta_tile(t - ph + kHalfTiles) + 2 * tid, r_pg, r_idx);
+        if (resolving && ph == 1) publish(t - ph + kHalfTiles, r_pg, r_idx);
         {
             const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
             bool rescale = false;
@@ -390,79 +423,62 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 0>{});
     }
 
-    // Epilogue: per-head output scale and lse (lanes l16 == 0 of the consumers).
+    // Epilogue: output scale and lse of each head (consumer lanes of row 0,
+    // one head each).
     const bool direct = p.S == 1;
-    if (consumer && l16 == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hl = 16 * wave + 4 * lg + r;
-            const int h = h0 + hl;
-            float scale, lse;
-            if (direct && p.sink) {
-                const float sk = p.sink[h] * kLog2e;
-                const float M = fmaxf(m_run[r], sk);
-                const float em = __builtin_amdgcn_exp2f(m_run[r] - M);
-                const float D = l_run[r] * em + __builtin_amdgcn_exp2f(sk - M);
-                scale = em / D;
-                lse = (M + __builtin_amdgcn_logf(D)) * kLn2;
-            } else if (l_run[r] > 0.f) {
-                scale = 1.f / l_run[r];
-                lse = (m_run[r] + __builtin_amdgcn_logf(l_run[r])) * kLn2;
-            } else {
-                scale = 0.f;
-                lse = -INFINITY;
-            }
-            fin[hl] = scale;
-            if (direct) {
-                if (p.lse) p.lse[(int64_t)b * p.H + h] = lse;
-            } else {
-                p.part_lse[((int64_t)b * p.H + h) * p.S + s] = lse;
-            }
+    if (consumer && lg == 0) {
+        const int h = h0 + hc;
+        float scale, lse;
+        if (direct && p.sink) {
+            const float M = fmaxf(m_run, sink_l2);
+            const float em = __builtin_amdgcn_exp2f(m_run - M);
+            const float D = l_run * em + __builtin_amdgcn_exp2f(sink_l2 - M);
+            scale = em * __builtin_amdgcn_rcpf(D);
+            lse = (M + __builtin_amdgcn_logf(D)) * kLn2;
+        } else if (l_run > 0.f) {
+            scale = __builtin_amdgcn_rcpf(l_run);
+            lse = (m_run + __builtin_amdgcn_logf(l_run)) * kLn2;
+        } else {
+            scale = 0.f;
+            lse = -INFINITY;
+        }
+        fin[hc] = scale;
+        if (direct) {
+            if (p.lse) p.lse[(int64_t)b * p.H + h] = lse;
+        } else {
+            p.part_lse[((int64_t)b * p.H + h) * p.S + s] = lse;
         }
     }
     __syncthreads();
 
-    // Output through LDS: lane holds O[16mt + 4lg + r][64w + 16nt + l16].
+    // Output through LDS as bf16 (the final output, or the split's partial):
+    // lane holds O[16mt + 4lg + r][64w + 16nt + l16].
+    constexpr int LD = L::stage_ld;
+    __bf16* st = reinterpret_cast<__bf16*>(smem + L::stage);        // [HG][520]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                st[(16 * mt + 4 * lg + r) * LD + 64 * wave + 16 * nt + l16] =
+                    (__bf16)(acc[mt][nt][r] * sc[r]);
+    }
+    __syncthreads();
+    uint16_t* dst;
+    int64_t row_stride;
     if (direct) {
-        constexpr int LD = L::stage_ld_bf16;
-        __bf16* st = reinterpret_cast<__bf16*>(smem + L::stage);    // [HG][520]
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    st[(16 * mt + 4 * lg + r) * LD + 64 * wave + 16 * nt + l16] =
-                        (__bf16)(acc[mt][nt][r] * sc[r]);
-        }
-        __syncthreads();
-        uint16_t* out = p.out + ((int64_t)b * p.H + h0) * kD;
-        for (int c = tid; c < HG * (kD / 8); c += kThreads) {
-            const int row = c >> 6, col = (c & 63) * 8;
-            *reinterpret_cast<bf16x8*>(out + (int64_t)row * kD + col) =
-                *reinterpret_cast<const bf16x8*>(&st[row * LD + col]);
-        }
+        dst = p.out + ((int64_t)b * p.H + h0) * kD;
+        row_stride = kD;
     } else {
-        constexpr int LD = L::stage_ld_f32;
-        float* st = reinterpret_cast<float*>(smem + L::stage);      // [HG][516]
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    st[(16 * mt + 4 * lg + r) * LD + 64 * wave + 16 * nt + l16] =
-                        acc[mt][nt][r] * sc[r];
-        }
-        __syncthreads();
-        for (int c = tid; c < HG * (kD / 4); c += kThreads) {
-            const int row = c >> 7, col = (c & 127) * 4;
-            const int64_t bh = (int64_t)b * p.H + h0 + row;
-            *reinterpret_cast<f32x4*>(p.part_o + (bh * p.S + s) * kD + col) =
-                *reinterpret_cast<const f32x4*>(&st[row * LD + col]);
-        }
+        dst = p.part_o + (((int64_t)b * p.H + h0) * p.S + s) * kD;
+        row_stride = (int64_t)p.S * kD;
+    }
+    for (int c = tid; c < HG * (kD / 8); c += kThreads) {
+        const int row = c >> 6, col = (c & 63) * 8;
+        *reinterpret_cast<bf16x8*>(dst + row * row_stride + col) =
+            *reinterpret_cast<const bf16x8*>(&st[row * LD + col]);
     }
 }
 
@@ -476,19 +492,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % p.H);
     const float* ls = p.part_lse + bh * p.S;
-    const float* po = p.part_o + bh * p.S * kD + threadIdx.x * 4;
+    const uint16_t* po = p.part_o + bh * p.S * kD + threadIdx.x * 4;
     float M = p.sink ? p.sink[h] : -INFINITY;
     float D = p.sink ? 1.f : 0.f;                    // e^{sink - M} with M = sink
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < p.S; s0 += kCombineBatch) {
         const int n = min(kCombineBatch, p.S - s0);
-        f32x4 v[kCombineBatch];
+        uint2 v[kCombineBatch];
         float l[kCombineBatch];
 #pragma unroll
         for (int j = 0; j < kCombineBatch; ++j) {
             l[j] = j < n ? ls[s0 + j] : -INFINITY;
-            v[j] = j < n ? *reinterpret_cast<const f32x4*>(po + (int64_t)(s0 + j) * kD)
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
+            v[j] = j < n ? *reinterpret_cast<const uint2*>(po + (int64_t)(s0 + j) * kD)
+                         : make_uint2(0u, 0u);
         }
         float cm = -INFINITY;
 #pragma unroll
@@ -502,7 +518,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
         for (int j = 0; j < kCombineBatch; ++j) {
             const float w = l[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((l[j] - M2) * kLog2e);
             D += w;
-            o += w * v[j];
+            const f32x4 pv = {__uint_as_float(v[j].x << 16), __uint_as_float(v[j].x & 0xFFFF0000u),
+                              __uint_as_float(v[j].y << 16), __uint_as_float(v[j].y & 0xFFFF0000u)};
+            o += w * pv;
         }
         M = M2;
     }

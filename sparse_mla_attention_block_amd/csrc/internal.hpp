@@ -32,25 +32,23 @@ constexpr int kKnLd = kD + 8;       // row-major K tile [32][520] bf16, double-b
 constexpr int kPLd = kTile + 8;     // probabilities    [HG][40] bf16
 constexpr int kMetaTiles = 32;      // resolved-entry ring: two halves of 16 tiles
 
-// LDS carve-up of the partial kernel (bytes).  One workgroup fills a CU's
-// register file, so LDS is not the occupancy limit: the epilogue stages the
-// whole output of the workgroup at once, over everything but `fin`.
+// LDS carve-up of the partial kernel (bytes).  The epilogue stages the
+// workgroup's whole bf16 output over everything but `fin`.
 template <int HG>
 struct Smem {
     static constexpr int fin = 0;                                  // [HG] f32
     static constexpr int flags = fin + HG * 4;                     // [4] int
     static constexpr int alpha = flags + 16;                       // [HG] f32
     static constexpr int pb = alpha + HG * 4;                      // [HG][40] bf16
-    static constexpr int kn = pb + HG * kPLd * 2;                  // [2][32][520] bf16
+    static constexpr int vmask = pb + HG * kPLd * 2;               // [32 tiles] u32
+    static constexpr int kn = vmask + kMetaTiles * 4;              // [2][32][520] bf16
     static constexpr int meta = kn + 2 * kTile * kKnLd * 2;        // [32 tiles][32][2] int64
     static constexpr int loop_end = meta + kMetaTiles * kTile * 16;
     static constexpr int stage = alpha;                            // epilogue staging
-    static constexpr int stage_ld_f32 = kD + 4;                    // floats per staged row
-    static constexpr int stage_ld_bf16 = kD + 8;                   // bf16 per staged row
-    static constexpr int stage_end = stage + HG * stage_ld_f32 * 4;
+    static constexpr int stage_ld = kD + 8;                        // bf16 per staged row
+    static constexpr int stage_end = stage + HG * stage_ld * 2;
     static constexpr int bytes = loop_end > stage_end ? loop_end : stage_end;
     static_assert(bytes <= 160 * 1024, "LDS");
-    static_assert(HG * stage_ld_bf16 * 2 <= HG * stage_ld_f32 * 4, "bf16 staging");
 };
 
 constexpr size_t lds_bytes_for(int hg) {
@@ -69,7 +67,7 @@ struct DecodeParams {
     const float* sink;          // [H] or null
     uint16_t* out;              // bf16 [B, H, 512] (direct output, S == 1)
     float* lse;                 // [B, H] or null (direct output, S == 1)
-    float* part_o;              // [B, H, S, 512] (S > 1)
+    uint16_t* part_o;           // bf16 [B, H, S, 512] (S > 1)
     float* part_lse;            // [B, H, S] (S > 1)
     int64_t num_blocks;
     int64_t bt_stride;
@@ -81,7 +79,7 @@ struct DecodeParams {
 };
 
 struct CombineParams {
-    const float* part_o;
+    const uint16_t* part_o;     // bf16 [B, H, S, 512]
     const float* part_lse;
     const float* sink;
     uint16_t* out;

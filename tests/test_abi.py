@@ -71,7 +71,7 @@ def test_plan_of_each_workload(ci):
     assert p.grid_partial == -(-units // 8) * 8 * p.head_groups
     assert p.block_partial == 512
     if S > 1:
-        assert p.workspace_bytes == c["B"] * c["H"] * S * 513 * 4
+        assert p.workspace_bytes == c["B"] * c["H"] * S * (512 * 2 + 4)
         assert p.grid_combine == c["B"] * c["H"]
     else:
         assert p.workspace_bytes == 0 and p.grid_combine == 0
@@ -120,7 +120,7 @@ def test_validation_errors():
 def test_workspace_bytes():
     d = _desc(4, 64, 512, 128)
     assert dsv4.dsv4_sparse_decode_workspace_bytes(d, 1) == 0
-    assert dsv4.dsv4_sparse_decode_workspace_bytes(d, 4) == 4 * 64 * 4 * 513 * 4
+    assert dsv4.dsv4_sparse_decode_workspace_bytes(d, 4) == 4 * 64 * 4 * (512 * 2 + 4)
     assert dsv4.dsv4_sparse_decode_workspace_bytes(_desc(0, 64, 1, 0), 4) == 0   # invalid
 
 
