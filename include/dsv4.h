@@ -41,7 +41,8 @@ extern "C" {
 typedef enum dsv4_status {
     DSV4_OK = 0,
     DSV4_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, bad shape/stride/alignment */
-    DSV4_ERR_NOT_SUPPORTED = 2,      /* a head count the kernels have no variant for      */
+    DSV4_ERR_NOT_SUPPORTED = 2,      /* a shape the kernels have no variant for (no valid
+                                        descriptor returns it at present)               */
     DSV4_ERR_WORKSPACE_TOO_SMALL = 3,
     DSV4_ERR_HIP = 4                 /* a kernel launch failed; see dsv4_last_error()     */
 } dsv4_status;
@@ -73,7 +74,7 @@ const char* dsv4_last_error(void);
 
 typedef struct dsv4_decode_desc {
     int32_t batch;               /* B: query tokens, one per sequence (s_q = 1), >= 1 */
-    int32_t num_heads;           /* H: multiple of 16, <= 128 (see NOT_SUPPORTED)   */
+    int32_t num_heads;           /* H: multiple of 16 in [16, 128]                   */
     int32_t topk;                /* main entries per token, >= 0                     */
     int32_t swa;                 /* sliding-window entries per token, >= 0           */
     int32_t block_size;          /* slots per page, >= 1                             */
@@ -103,8 +104,11 @@ typedef struct dsv4_plan {
 } dsv4_plan;
 
 /* Plan a decode without launching anything: validates the descriptor
- * (pointers other than workspace are not looked at) and picks the split
- * count.  num_splits = 0 lets the selector choose:
+ * (pointers other than workspace are not looked at) and picks the head
+ * grouping and the split count.  Heads per workgroup: the largest multiple
+ * of 16 that divides H, at most 64, for which B * S * head_groups >= 256
+ * (one workgroup per compute unit), else 16; S is chosen for each candidate
+ * grouping as below.  num_splits = 0 lets the selector choose:
  *   B >= 256                 -> 1 (one workgroup per token already fills the
  *                               chip; SGLang PR #26383 page, implementation
  *                               item 3: no split-K at >= 256 tokens);

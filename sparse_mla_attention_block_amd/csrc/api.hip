@@ -74,30 +74,31 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         return fail(DSV4_ERR_INVALID_ARGUMENT, "topk_idx_stride %lld < topk + swa %lld",
                     (long long)idx_stride, (long long)kt);
 
-    const int groups = (int)ceil_div(d->num_heads, kMaxHeadsPerGroup);
-    const int hg = d->num_heads / groups;
-    if (hg * groups != d->num_heads || hg % 16)
-        return fail(DSV4_ERR_NOT_SUPPORTED,
-                    "num_heads %d cannot be cut into equal groups of a multiple of 16 heads "
-                    "(at most %d)", d->num_heads, kMaxHeadsPerGroup);
-
-    int S;
-    if (num_splits == 0) {
-        if (d->batch >= 256) {
-            S = 1;
-        } else {
-            const int64_t cap = kt <= 1024 ? 4 : 32;
-            int64_t want = ceil_div(kCUs, (int64_t)d->batch * groups);
-            const int64_t lim = cap < ceil_div(kt, kTile) ? cap : ceil_div(kt, kTile);
-            if (want > lim) want = lim;
-            if (want < 1) want = 1;
-            S = (int)want;
-        }
-    } else if (num_splits < 1 || num_splits > kMaxSplits) {
+    // Heads per workgroup: a multiple of 16 that divides H, at most 64.  The
+    // largest such group is tried first; while the grid (B x S x groups)
+    // would leave CUs idle, the next smaller group is used, since a small
+    // grid's time is its per-workgroup latency and fewer heads per
+    // workgroup shorten every tile step.
+    if (num_splits != 0 && (num_splits < 1 || num_splits > kMaxSplits))
         return fail(DSV4_ERR_INVALID_ARGUMENT, "num_splits must be 0 (auto) or in [1, %d] (got %d)",
                     kMaxSplits, num_splits);
-    } else {
-        S = num_splits;
+    auto pick_splits = [&](int groups) -> int {
+        if (num_splits != 0) return num_splits;
+        if (d->batch >= 256) return 1;
+        const int64_t cap = kt <= 1024 ? 4 : 32;
+        int64_t want = ceil_div(kCUs, (int64_t)d->batch * groups);
+        const int64_t lim = cap < ceil_div(kt, kTile) ? cap : ceil_div(kt, kTile);
+        if (want > lim) want = lim;
+        if (want < 1) want = 1;
+        return (int)want;
+    };
+    int hg = 0, groups = 0, S = 0;
+    for (int cand = kMaxHeadsPerGroup; cand >= 16; cand -= 16) {
+        if (d->num_heads % cand) continue;
+        hg = cand;
+        groups = d->num_heads / cand;
+        S = pick_splits(groups);
+        if ((int64_t)d->batch * S * groups >= kCUs) break;
     }
     const int64_t units = (int64_t)d->batch * S;
     const int64_t grid = ceil_div(units, kXcds) * kXcds * groups;

@@ -11,27 +11,28 @@
 //     masked or -inf score contributes exactly zero to the running sum.
 //
 // One workgroup = 8 waves serves one (token b, split s, head group g) and
-// walks its slice of the token's entry list in tiles of 32 cache rows.
-//   * Resolution (index -> page via the block table -> byte offsets) of 16
-//     tiles at a time, one entry per lane, into an LDS ring; the next half
-//     is resolved in steps spread over two tile periods so its dependent
-//     loads overlap compute.
-//   * Waves 4..7 ("producers", 8 lanes per cache row) keep the raw bytes of
-//     the next two tiles in flight in registers, dequantise FP8 x 2^(code-127)
-//     to bf16 and store
-//     tile t+1 row-major into one half of a double-buffered LDS K tile while
-//   * waves 0..3 ("consumers", one per 16-head MFMA row tile) run QK of tile
-//     t on bf16 MFMA 16x16x32 (q held in registers) fused with the online
-//     softmax (DPP row reductions, lazy rescaling: the running max only moves
-//     when a score exceeds it by more than 2^8), writing bf16 probabilities;
-//   * then all 8 waves run PV on bf16 MFMA, wave w owning output dims
-//     [64w, 64w+64); the V operand comes straight from the row-major K tile
-//     through the gfx950 LDS transpose read, so no transposed copy is kept.
-// Rows that do not take part are stored as zeros, so a NaN in the cache can
-// never reach an MFMA.  The running sum takes the fp32 probabilities, the PV
-// operand their bf16 rounding.  With one split the epilogue folds the sink in
-// and writes bf16 output and lse; with several it writes the split's
-// normalised fp32 partial and lse.  Both leave through LDS as 16-byte stores.
+// walks its slice of the token's entry list in tiles of 32 cache rows, as a
+// software pipeline with one barrier per step.  In step t:
+//   * waves 0..3 ("consumers", one per 16-head MFMA tile) run QK of tile t
+//     on bf16 MFMA 16x16x32 (q held in registers, S^T = K q^T so each lane
+//     holds 8 scores of one head) fused with the online softmax (cross-row
+//     permlane reductions, lazy rescaling: the running max only moves when a
+//     score exceeds it by more than 2^8), writing bf16 probabilities;
+//   * waves 4..7 ("producers", 8 lanes per cache row) dequantise tile t+1
+//     (FP8 x 2^(code-127) -> bf16 in one scaled convert per 2 values) into
+//     one of three LDS K buffers and issue the loads of tile t+3, keeping two
+//     tiles of raw bytes in flight in registers;
+//   * all 8 waves run PV of tile t-1 on bf16 MFMA, wave w owning output dims
+//     [64w, 64w+64); the V operand comes straight from the K tile through
+//     the gfx950 LDS transpose read, so no transposed copy is kept.
+// Entry resolution (index -> page via the block table -> row addresses) of
+// the first 32 tiles happens up front, into an LDS ring with a per-tile
+// bit mask of the rows that take part; longer splits resolve 16 more tiles
+// at a time inside the loop.  Rows that take no part read a zero row, so a
+// NaN in the cache can never reach an MFMA.  The running sum takes the fp32
+// probabilities, the PV operand their bf16 rounding.  With one split the
+// epilogue folds the sink in and writes bf16 output and lse; with several it
+// writes the split's normalised bf16 partial and lse.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -43,42 +44,46 @@ namespace dsv4 {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.f;   // log2 units a score may exceed the running max by
 constexpr int kHalfTiles = kMetaTiles / 2;
 
-// 2^(code-127) as an fp32 value: UE8M0 code 0 is the subnormal 2^-127 and
-// code 255 is NaN (the E8M0 encoding).
-__device__ __forceinline__ float ue8m0_to_float(uint32_t code) {
-    const uint32_t bits = code == 0u ? 0x00400000u : (code == 255u ? 0x7FC00000u : code << 23);
-    return __uint_as_float(bits);
+// Two FP8 E4M3FN bytes of `packed` (bytes 0-1, or 2-3 with HI) times a power
+// of two, as two bf16, in one gfx950 scaled convert.  The instruction takes
+// only the exponent field of its fp32 scale operand, so UE8M0 code c is
+// passed as the float bits c << 23: code 0 is 2^-127 and 255 is NaN, the
+// E8M0 meanings.  For every FP8 byte and scale codes from 0 to 255 the
+// result equals the bf16 rounding of the exact product (checked on gfx950
+// against an exact decoder).  Inline asm: the compiler's builtin for this
+// instruction returns the low byte's value in both halves.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_scaled_pk(uint32_t packed, float scale) {
+    uint32_t r;
+    if (HI)
+        asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2 op_sel:[1,0,0]" : "=v"(r) : "v"(packed), "v"(scale));
+    else
+        asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2" : "=v"(r) : "v"(packed), "v"(scale));
+    return r;
 }
 
-// 8 E4M3FN bytes times a power-of-two scale, as 8 bf16.  The gfx950 convert
-// decodes OCP E4M3FN exactly to fp32; the product is exact and so is its
-// bf16 rounding for every value a 4-bit-significand FP8 times 2^k can take
-// inside bf16's normal range.
-__device__ __forceinline__ bf16x8 dequant8(uint2 raw, float scale) {
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(raw.x, false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(raw.x, true);
-    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(raw.y, false);
-    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(raw.y, true);
-    bf16x8 v;
-    v[0] = (__bf16)(a[0] * scale);
-    v[1] = (__bf16)(a[1] * scale);
-    v[2] = (__bf16)(b[0] * scale);
-    v[3] = (__bf16)(b[1] * scale);
-    v[4] = (__bf16)(c[0] * scale);
-    v[5] = (__bf16)(c[1] * scale);
-    v[6] = (__bf16)(d[0] * scale);
-    v[7] = (__bf16)(d[1] * scale);
-    return v;
+// 8 E4M3FN bytes times 2^(code-127), as 8 bf16.
+__device__ __forceinline__ bf16x8 dequant8(uint2 raw, uint32_t code) {
+    const float scale = __uint_as_float(code << 23);
+    return __builtin_bit_cast(bf16x8, u32x4{cvt_scaled_pk<false>(raw.x, scale),
+                                            cvt_scaled_pk<true>(raw.x, scale),
+                                            cvt_scaled_pk<false>(raw.y, scale),
+                                            cvt_scaled_pk<true>(raw.y, scale)});
 }
+
+// Source of rows that take no part and of tiles past the end of a split: 576
+// zero data bytes and a zero scale word, which dequantise to exact zeros, so
+// a NaN anywhere in the cache can never reach an MFMA.
+__device__ __attribute__((aligned(64))) const uint8_t kZeroRow[kRowData + 64] = {};
 
 // Reductions over the 16 lanes of a DPP row (lanes sharing lane >> 4):
 // quad xor 1, quad xor 2, half-row mirror, row mirror.
@@ -108,82 +113,119 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const __bf16* p) {
         (__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// Producer lane pl (0..255) owns row pl/8 of a tile and, of the row's 72
-// eight-byte chunks (576 data bytes), chunks l8 + 8j for j = 0..8, l8 = pl%8:
-// j < 7 are NoPE chunks (8 FP8 dims scaled by code j of the row's scale
-// word), j = 7, 8 are RoPE chunks (4 bf16 dims each).  Every lane therefore
-// runs the same instructions; a wave reads 64 contiguous bytes from each of
-// 8 rows per load.  The raw chunks of a tile live in rr[O .. O+17] and the
-// row's scale word in rr[O+18 .. O+19].  The loads are unconditional (a row
-// that takes no part reads the pool's first row and is zeroed when stored),
-// so they issue back to back.
-// meta row: [byte offset of the row's data (-1 = the row takes no part),
-//            byte offset of its scale word].
-constexpr int kChunks = 9;
-
-template <int O>
-__device__ __forceinline__ void load_patch(const DecodeParams& p, const int64_t* meta, int prow,
-                                           int l8, uint32_t (&rr)[64]) {
-    const int64_t d = max(meta[2 * prow], (int64_t)0);
-    const uint8_t* src = p.kv + d + 8 * l8;
-    const uint2 sw = *reinterpret_cast<const uint2*>(p.kv + meta[2 * prow + 1]);
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src + 64 * j);
-        rr[O + 2 * j] = v.x;
-        rr[O + 2 * j + 1] = v.y;
-    }
-    rr[O + 18] = sw.x;
-    rr[O + 19] = sw.y;
+// K tile layout: row-major, 512 bf16 (1024 B) per row, the row's 64
+// sixteen-byte units permuted by XOR with swz(row) (bits of the row number
+// moved to unit bits 3, 1-2 and 4).  The permutation was chosen by measuring
+// the LDS bank-conflict counter for the kernel's four access patterns on
+// gfx950: the QK fragment reads (16 rows, one unit each, per 16 lanes), the
+// PV transpose reads (4 rows x four 8-byte pieces per 16 lanes), and the
+// producers' 16-byte and 8-byte stores (rows r and r+4 per 16 lanes).
+__device__ __forceinline__ int swz(int row) {
+    return 8 * (row & 1) + 2 * ((row >> 1) & 3) + 16 * ((row >> 3) & 1);
 }
 
-// Dequantises the chunks into the row-major K tile.
+// Element offset of element `elem` of row `row` in a K tile.
+__device__ __forceinline__ int kofs(int row, int elem) {
+    return row * kD + ((((elem >> 3) ^ swz(row))) << 3) + (elem & 7);
+}
+
+// Producer lane l of producer wave v owns row 8v + l/16 + 4((l/8)%2) of a
+// tile (so 16 lanes store rows r and r+4) and, of the row's 72 eight-byte
+// chunks (576 data bytes), chunks l8 + 8j for j = 0..8, l8 = l%8: j < 7 are
+// NoPE chunks (8 FP8 dims scaled by code j of the row's scale word), j = 7, 8
+// are RoPE chunks (4 bf16 dims each).  Every lane therefore runs the same
+// instructions; a wave reads 64 contiguous bytes from each of 8 rows per
+// load.  The raw chunks of a tile live in rr[O .. O+17] and the row's scale
+// word in rr[O+18 .. O+19].  The loads are unconditional: a row that takes no
+// part, or a tile past the end of the split, reads the zero row.  With no
+// branch around them the compiler can count the loads in flight and wait for
+// one tile's loads while the next tile's are still outstanding.
+// meta row: [address of the row's 576 data bytes, address of its scale word]
+// (the zero row for a row that takes no part).
+constexpr int kChunks = 9;
+
+// Global-memory pointers (address space 1), so the loads are global loads
+// (counted by vmcnt alone) rather than flat ones.
+typedef const __attribute__((address_space(1))) uint8_t gbyte;
+typedef const __attribute__((address_space(1))) uint64_t gu64;
+
+struct PatchSrc {
+    gbyte* data;
+    gbyte* scale;
+};
+
+// A producer lane's row addresses, read as one 16-byte LDS word (the slot
+// always exists; a dead tile's stale entry is replaced after the read).
+__device__ __forceinline__ PatchSrc patch_src(const int64_t* meta, int prow, bool live) {
+    const i64x2 m = *reinterpret_cast<const i64x2*>(meta + 2 * prow);
+    const int64_t z = reinterpret_cast<int64_t>(kZeroRow);
+    return PatchSrc{(gbyte*)(live ? m[0] : z), (gbyte*)(live ? m[1] : z + kRowData)};
+}
+
 template <int O>
-__device__ __forceinline__ void store_patch(const uint32_t (&rr)[64], const int64_t* meta, int prow,
-                                            int l8, __bf16* Kn) {
-    const bool ok = meta[2 * prow] >= 0;
-    const uint64_t sw = ok ? ((uint64_t)rr[O + 19] << 32 | rr[O + 18]) : 0x7F7F7F7F7F7F7F7Full;
-    __bf16* row = Kn + prow * kKnLd;
+__device__ __forceinline__ void load_patch(PatchSrc a, int l8, uint32_t (&rr)[64]) {
+    gbyte* src = a.data + 8 * l8;
+    const uint64_t sw = *(gu64*)a.scale;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+        const uint64_t v = *(gu64*)(src + 64 * j);
+        rr[O + 2 * j] = (uint32_t)v;
+        rr[O + 2 * j + 1] = (uint32_t)(v >> 32);
+    }
+    rr[O + 18] = (uint32_t)sw;
+    rr[O + 19] = (uint32_t)(sw >> 32);
+}
+
+// Dequantises the chunks into the K tile.
+template <int O>
+__device__ __forceinline__ void store_patch(const uint32_t (&rr)[64], int prow, int l8,
+                                            __bf16* Kt) {
+    const uint64_t sw = (uint64_t)rr[O + 19] << 32 | rr[O + 18];
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
-        const uint2 raw = ok ? make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]) : make_uint2(0u, 0u);
-        const float sc = ue8m0_to_float((uint32_t)(sw >> (8 * j)) & 0xFFu);
-        *reinterpret_cast<bf16x8*>(row + 64 * j + 8 * l8) = dequant8(raw, sc);
+        const uint2 raw = make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]);
+        *reinterpret_cast<bf16x8*>(Kt + kofs(prow, 64 * j + 8 * l8)) =
+            dequant8(raw, (uint32_t)(sw >> (8 * j)) & 0xFFu);
     }
 #pragma unroll
     for (int j = 7; j < kChunks; ++j) {
-        const uint2 raw = ok ? make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]) : make_uint2(0u, 0u);
-        *reinterpret_cast<uint2*>(row + kDNope + 32 * (j - 7) + 4 * l8) = raw;
+        const uint2 raw = make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]);
+        *reinterpret_cast<uint2*>(Kt + kofs(prow, kDNope + 32 * (j - 7) + 4 * l8)) = raw;
     }
 }
 
-// Entry resolution helpers: effective position -> index -> page -> scale word.
+// Entry resolution helpers: effective position -> index -> page.  Both loads
+// are unconditional (an out-of-range position reads column 0, a masked index
+// block 0 of the row's table) and the result is selected afterwards, so the
+// loop they sit in has no branch around a load.
 __device__ __forceinline__ int32_t load_index(const DecodeParams& p, int b, int vl, int hi,
                                               int pos) {
-    if (pos >= hi) return -1;
-    const int col = pos < vl ? pos : p.topk + (pos - vl);
-    return p.idx[(int64_t)b * p.idx_stride + col];
+    const bool in = pos < hi;
+    const int col = in ? (pos < vl ? pos : p.topk + (pos - vl)) : 0;
+    const int32_t v = p.idx[(int64_t)b * p.idx_stride + col];
+    return in ? v : -1;
 }
 
 __device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, int b, int32_t idx) {
-    if (idx < 0) return -1;
-    const int64_t blk = idx / p.bs;
+    const bool ok = idx >= 0;
+    const int64_t blk = (ok ? idx : 0) / p.bs;
     if (p.bt) {
-        if (blk >= p.max_blocks) return -1;
-        const int32_t pg = p.bt[(int64_t)b * p.bt_stride + blk];
-        return (pg >= 0 && pg < p.num_blocks) ? pg : -1;
+        const bool inb = ok && blk < p.max_blocks;
+        const int32_t pg = p.bt[(int64_t)b * p.bt_stride + (inb ? blk : 0)];
+        return (inb && pg >= 0 && pg < p.num_blocks) ? pg : -1;
     }
-    return blk < p.num_blocks ? blk : -1;
+    return (ok && blk < p.num_blocks) ? blk : -1;
 }
 
-// Data and scale-word byte offsets of the row at (page, idx % bs); a row that
-// takes no part gets data offset -1 and scale offset 0 (the pool's first
-// bytes, read and discarded).
+// Data and scale-word addresses of the row at (page, idx % bs); the zero row
+// for a row that takes no part.
 __device__ __forceinline__ void write_meta(const DecodeParams& p, int64_t* row, int64_t page,
                                            int32_t idx) {
     const int64_t off = idx % p.bs;
-    row[0] = page >= 0 ? page * p.page_stride + off * kRowData : -1;
-    row[1] = page >= 0 ? page * p.page_stride + (int64_t)p.bs * kRowData + off * kRowScale : 0;
+    const uint8_t* pg = p.kv + page * p.page_stride;
+    row[0] = reinterpret_cast<int64_t>(page >= 0 ? pg + off * kRowData : kZeroRow);
+    row[1] = reinterpret_cast<int64_t>(
+        page >= 0 ? pg + (int64_t)p.bs * kRowData + off * kRowScale : kZeroRow + kRowData);
 }
 
 // Reductions across the four 16-lane rows of a wave.  v_permlane16_swap
@@ -215,11 +257,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     static_assert(HG % 16 == 0 && HG <= kMaxHeadsPerGroup, "head group");
     using L = Smem<HG>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::bytes];
-    __bf16* Kn = reinterpret_cast<__bf16*>(smem + L::kn);          // [2][32][520]
-    __bf16* Pb = reinterpret_cast<__bf16*>(smem + L::pb);          // [HG][40]
-    float* alpha_s = reinterpret_cast<float*>(smem + L::alpha);
+    __bf16* Kn = reinterpret_cast<__bf16*>(smem + L::kn);          // [3][32][512], swizzled
+    __bf16* Pb = reinterpret_cast<__bf16*>(smem + L::pb);          // [2][HG][40]
+    float* alpha_s = reinterpret_cast<float*>(smem + L::alpha);    // [2][HG]
     float* fin = reinterpret_cast<float*>(smem + L::fin);
-    int* flags = reinterpret_cast<int*>(smem + L::flags);
+    int* flags = reinterpret_cast<int*>(smem + L::flags);          // [2][4]
     uint32_t* vmask = reinterpret_cast<uint32_t*>(smem + L::vmask);  // [32 tiles]
     int64_t* meta = reinterpret_cast<int64_t*>(smem + L::meta);    // [32 tiles][32][2]
 
@@ -252,10 +294,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
     const bool consumer = wave < MT;
     const bool producer = wave >= 4;
-    const int ptid = tid - 4 * 64;
-    const int prow = ptid >> 3, l8 = ptid & 7;   // producer: tile row, chunk lane
+    // Producer: tile row and chunk lane.
+    const int prow = 8 * (wave - 4) + (lane >> 4) + 4 * ((lane >> 3) & 1), l8 = lane & 7;
     const int hc = 16 * wave + l16;              // consumer lane's head (within the group)
     auto meta_tile = [&](int t) { return meta + (t % kMetaTiles) * kTile * 2; };
+    auto kbuf = [&](int t) { return Kn + (t % kKBufs) * (kTile * kD); };
 
     // One 64-register array per lane, used by role: consumers keep the q
     // row of their head in it (lane (l16, lg) holds dims 32*ks + 8*lg .. +7
@@ -277,156 +320,228 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         if (p.sink) sink_l2 = p.sink[h0 + hc] * kLog2e;
     }
 
-    // Resolution of 16 tiles: one entry per lane, then a per-tile bit mask of
-    // the rows that take part (each wave covers two tiles).
-    auto publish = [&](int first_tile, int64_t page, int32_t idx) {
-        write_meta(p, meta_tile(first_tile) + 2 * tid, page, idx);
-        const uint64_t bits = __builtin_amdgcn_ballot_w64(page >= 0);
-        if (lane == 0) {
-            vmask[(first_tile + 2 * wave) % kMetaTiles] = (uint32_t)bits;
-            vmask[(first_tile + 2 * wave + 1) % kMetaTiles] = (uint32_t)(bits >> 32);
-        }
-    };
+    // Resolution of the first 32 tiles (the whole ring): two entries per
+    // thread, then a per-tile bit mask of the rows that take part (wave w
+    // covers tiles 2w, 2w+1 and 16+2w, 17+2w).  Later tiles are resolved 16 at
+    // a time inside the loop, which only splits longer than 32 tiles reach.
     {
-        const int32_t idx = load_index(p, b, vl, hi, lo + tid);
-        publish(0, lookup_page(p, b, idx), idx);
+        const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
+        const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
+        const int64_t g0 = lookup_page(p, b, i0);
+        const int64_t g1 = lookup_page(p, b, i1);
+        write_meta(p, meta + 2 * tid, g0, i0);
+        write_meta(p, meta + 2 * (kThreads + tid), g1, i1);
+        const uint64_t b0 = __builtin_amdgcn_ballot_w64(g0 >= 0);
+        const uint64_t b1 = __builtin_amdgcn_ballot_w64(g1 >= 0);
+        if (lane == 0) {
+            vmask[2 * wave] = (uint32_t)b0;
+            vmask[2 * wave + 1] = (uint32_t)(b0 >> 32);
+            vmask[kHalfTiles + 2 * wave] = (uint32_t)b1;
+            vmask[kHalfTiles + 2 * wave + 1] = (uint32_t)(b1 >> 32);
+        }
     }
     __syncthreads();
 
     if (producer) {
-        if (ntiles > 0) load_patch<0>(p, meta_tile(0), prow, l8, rr);
-        if (ntiles > 1) load_patch<32>(p, meta_tile(1), prow, l8, rr);
-        if (ntiles > 0) store_patch<0>(rr, meta_tile(0), prow, l8, Kn);
-        if (ntiles > 2) load_patch<0>(p, meta_tile(2), prow, l8, rr);
+        load_patch<0>(patch_src(meta_tile(0), prow, ntiles > 0), l8, rr);
+        load_patch<32>(patch_src(meta_tile(1), prow, ntiles > 1), l8, rr);
+        const PatchSrc a2 = patch_src(meta_tile(2), prow, ntiles > 2);
+        store_patch<0>(rr, prow, l8, kbuf(0));
+        load_patch<0>(a2, l8, rr);
     }
     __syncthreads();
 
     // Online-softmax state of a consumer lane's head, in base-2 units
     // (replicated over the lane's four 16-lane rows).
     float m_run = -INFINITY, l_run = 0.f;
+    // PV accumulators: wave w owns output dims [64w, 64w+64).  acc[mt][nt]
+    // is a 16-dim x 16-head block of O^T; lane (l16, lg) holds head 16mt + l16
+    // at dims 64w + 16nt + 4lg + r, r = 0..3.
     f32x4 acc[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Staged resolution of the next half (16 tiles), one entry per lane.
-    int32_t r_idx = -1;
-    int64_t r_pg = -1;
-
-    // One tile period; rr[O..O+19] holds tile t+1's raw bytes and receives
-    // tile t+3's (O = 32 for even t, 0 for odd t).
-    auto step = [&](int t, auto off) __attribute__((always_inline)) {
-        constexpr int O = decltype(off)::value;
+    // Staged resolution of the next half (16 tiles, from tile 32 on) by
+    // waves 0..3, two entries per lane: entry 128w + l (tiles 4w, 4w+1) and 128w + 64 + l
+    // (tiles 4w+2, 4w+3).  Phase 0 loads the raw indices, phase 1 masks them
+    // and loads the raw block-table entries, phase 2 turns them into pages and
+    // publishes the offsets and tile masks; each load's result is first used
+    // one step (one barrier) after it is issued.
+    int32_t r_i0 = 0, r_i1 = 0, r_p0 = 0, r_p1 = 0;
+    auto raw_index = [&](int pos) {
+        const int cpos = pos < hi ? pos : lo;
+        const int col = cpos < vl ? cpos : p.topk + (cpos - vl);
+        return p.idx[(int64_t)b * p.idx_stride + (pos < hi ? col : 0)];
+    };
+    auto bt_col = [&](int32_t idx) {
+        const int64_t blk = idx / p.bs;
+        return idx >= 0 && blk < p.max_blocks ? blk : (int64_t)0;
+    };
+    auto page_of = [&](int32_t idx, int32_t raw) -> int64_t {
+        if (idx < 0) return -1;
+        const int64_t blk = idx / p.bs;
+        if (p.bt) return blk < p.max_blocks && raw >= 0 && raw < p.num_blocks ? raw : -1;
+        return blk < p.num_blocks ? blk : -1;
+    };
+    auto resolve_stage = [&](int t) __attribute__((always_inline)) {
         const int ph = t % kHalfTiles;
-        const bool resolving = t - ph + kHalfTiles < ntiles;   // a next half exists
-        const int half_base = lo + (t - ph + kHalfTiles) * kTile;
-        // ---- B: QK + softmax (consumers) | dequant t+1, load t+3 (producers)
-        if (resolving && ph == 0) r_idx = load_index(p, b, vl, hi, half_base + tid);
-        if (consumer) {
-            // S^T = K q^T: A operand = K rows (entries), B operand = q (heads).
-            const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-            const __bf16* k0 = &K[l16 * kKnLd + 8 * lg];
-            const __bf16* k1 = &K[(16 + l16) * kKnLd + 8 * lg];
-#pragma unroll
-            for (int ks = 0; ks < 16; ++ks) {
-                const bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(k0 + 32 * ks);
-                const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(k1 + 32 * ks);
-                const bf16x8 qb = __builtin_bit_cast(
-                    bf16x8, u32x4{rr[4 * ks], rr[4 * ks + 1], rr[4 * ks + 2], rr[4 * ks + 3]});
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb0, qb, s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb1, qb, s1, 0, 0, 0);
+        const int nxt = t - ph + kHalfTiles;      // first tile of the next half
+        if (nxt < kMetaTiles || nxt >= ntiles || ph >= 3) return;
+        const int e0 = lo + nxt * kTile + 128 * wave + lane;
+        if (ph == 0) {
+            r_i0 = raw_index(e0);
+            r_i1 = raw_index(e0 + 64);
+        } else if (ph == 1) {
+            r_i0 = e0 < hi ? r_i0 : -1;
+            r_i1 = e0 + 64 < hi ? r_i1 : -1;
+            if (p.bt) {
+                r_p0 = p.bt[(int64_t)b * p.bt_stride + bt_col(r_i0)];
+                r_p1 = p.bt[(int64_t)b * p.bt_stride + bt_col(r_i1)];
             }
-            // lane holds the scores of head hc for rows 4lg + r (s0) and 16 + 4lg + r (s1).
-            const uint32_t vm = vmask[t % kMetaTiles];
-            float x[8];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x[r] = (vm >> (4 * lg + r)) & 1u ? s0[r] * p.qk_scale_log2 : -INFINITY;
-                x[4 + r] = (vm >> (16 + 4 * lg + r)) & 1u ? s1[r] * p.qk_scale_log2 : -INFINITY;
-                mx = fmaxf(mx, fmaxf(x[r], x[4 + r]));
-            }
-            mx = xrow_max4(mx);
-            // Move the running max only when a score exceeds it by more than
-            // the slack (always on the first valid score).
-            const bool move = mx > m_run + kRescaleSlack;
-            const float m_use = move ? mx : m_run;
-            const float a = move ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;   // 0 if m_run = -inf
-            float e[8], psum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                e[i] = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m_use);
-                psum += e[i];
-            }
-            l_run = l_run * a + xrow_sum4(psum);
-            m_run = m_use;
-            bf16x8 pv;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pv[i] = (__bf16)e[i];
-            __bf16* prow_p = Pb + hc * kPLd + 4 * lg;
-            *reinterpret_cast<uint2*>(prow_p) = __builtin_bit_cast(
-                uint2, __builtin_shufflevector(pv, pv, 0, 1, 2, 3));
-            *reinterpret_cast<uint2*>(prow_p + 16) = __builtin_bit_cast(
-                uint2, __builtin_shufflevector(pv, pv, 4, 5, 6, 7));
-            if (lg == 0) alpha_s[hc] = a;
-            const bool any = __builtin_amdgcn_ballot_w64(move) != 0;
-            if (lane == 0) flags[wave] = any ? 1 : 0;
-        }
-        if (producer) {
-            if (t + 1 < ntiles)
-                store_patch<O>(rr, meta_tile(t + 1), prow, l8, Kn + ((t + 1) & 1) * kTile * kKnLd);
-            if (t + 3 < ntiles) load_patch<O>(p, meta_tile(t + 3), prow, l8, rr);
-        }
-        __syncthreads();
-
-        // ---- C: PV (all waves) into output dims [64w, 64w+64).
-        if (resolving && ph == 0) r_pg = lookup_page(p, b, r_idx);
-        if (resolving && ph == 1) publish(t - ph + kHalfTiles, r_pg, r_idx);
-        {
-            const __bf16* K = Kn + (t & 1) * kTile * kKnLd;
-            bool rescale = false;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) rescale |= flags[mt] != 0;
-            bf16x8 pa[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                pa[mt] = *reinterpret_cast<const bf16x8*>(&Pb[(16 * mt + l16) * kPLd + 8 * lg]);
-                if (rescale) {
-                    const f32x4 al = *reinterpret_cast<const f32x4*>(&alpha_s[16 * mt + 4 * lg]);
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] *= al;
-                }
-            }
-            // V operand: lane j of 16-lane group lg points at rows 8lg + 4h + j/4,
-            // dims dimb + 4(j%4); the transpose read hands lane i dim dimb + i of
-            // rows 8lg + 4h .. +3.
-            const __bf16* vrow = &K[(8 * lg + (l16 >> 2)) * kKnLd + 64 * wave + 4 * (l16 & 3)];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const i16x4 v0 = lds_read_tr16(vrow + 16 * nt);
-                const i16x4 v1 = lds_read_tr16(vrow + 4 * kKnLd + 16 * nt);
-                const bf16x8 vb = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, acc[mt][nt],
-                                                                          0, 0, 0);
+        } else {
+            const int64_t pg0 = page_of(r_i0, r_p0), pg1 = page_of(r_i1, r_p1);
+            int64_t* m = meta_tile(nxt) + 2 * (128 * wave + lane);
+            write_meta(p, m, pg0, r_i0);
+            write_meta(p, m + 2 * 64, pg1, r_i1);
+            const uint64_t b0 = __builtin_amdgcn_ballot_w64(pg0 >= 0);
+            const uint64_t b1 = __builtin_amdgcn_ballot_w64(pg1 >= 0);
+            if (lane == 0) {
+                uint32_t* vmk = vmask + (nxt + 4 * wave) % kMetaTiles;
+                vmk[0] = (uint32_t)b0;
+                vmk[1] = (uint32_t)(b0 >> 32);
+                vmk[2] = (uint32_t)b1;
+                vmk[3] = (uint32_t)(b1 >> 32);
             }
         }
-        __syncthreads();
     };
 
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, std::integral_constant<int, 32>{});
-        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 0>{});
-    }
+    // PV of tile k (all waves): O^T += V^T P^T with V = the K tile.  The k
+    // index of the MFMA runs over the tile's entries in the order a QK lane
+    // holds them: k = 8g + i is entry 4g + i (i < 4) or 16 + 4g + i - 4.  The
+    // B operand (P^T) is then the QK lane's 8 probabilities as written; the A
+    // operand (V^T, rows = 16 dims) comes from the K tile through the LDS
+    // transpose read: lane j of 16-lane group g addresses entry 4g + j/4 (and
+    // 16 + 4g + j/4) at dims base + 4(j%4), so lane i receives dim base + i
+    // of entries 4g .. 4g+3 (16 + 4g .. 16 + 4g+3).
+    auto pv = [&](int k) __attribute__((always_inline)) {
+        const __bf16* K = kbuf(k);
+        const __bf16* P = Pb + (k & 1) * (HG * kPLd);
+        const int* fl = flags + (k & 1) * 4;
+        bool rescale = false;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) rescale |= fl[mt] != 0;
+        if (rescale) {
+            const float* al = alpha_s + (k & 1) * HG;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float a = al[16 * mt + l16];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) acc[mt][nt] *= a;
+            }
+        }
+        bf16x8 pa[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            pa[mt] = *reinterpret_cast<const bf16x8*>(&P[(16 * mt + l16) * kPLd + 8 * lg]);
+        const int vr = 4 * lg + (l16 >> 2);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int d = 64 * wave + 16 * nt + 4 * (l16 & 3);
+            const i16x4 v0 = lds_read_tr16(K + kofs(vr, d));
+            const i16x4 v1 = lds_read_tr16(K + kofs(16 + vr, d));
+            const bf16x8 vb = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pa[mt], acc[mt][nt],
+                                                                      0, 0, 0);
+        }
+    };
 
-    // Epilogue: output scale and lse of each head (consumer lanes of row 0,
-    // one head each).
+    // QK + online softmax of tile t (consumer waves).
+    auto qk = [&](int t) __attribute__((always_inline)) {
+        // S^T = K q^T: A operand = K rows (entries), B operand = q (heads).
+        // Four accumulator chains (rows 0-15 / 16-31, even / odd k-steps);
+        // K fragments are read four k-steps ahead of their MFMAs, an order
+        // pinned with scheduling-group barriers so LDS latency stays hidden.
+        const __bf16* K = kbuf(t);
+        f32x4 sa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 sb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // Lane (l16, lg) reads rows l16 and 16 + l16 (same swizzle), elements
+        // 32ks + 8lg.
+        auto kfrag = [&](int row, int ks) {
+            return *reinterpret_cast<const bf16x8*>(K + kofs(row, 32 * ks + 8 * lg));
+        };
+        constexpr int kAhead = 4;
+        bf16x8 fa[kAhead], fb[kAhead];
+#pragma unroll
+        for (int ks = 0; ks < kAhead; ++ks) {
+            fa[ks] = kfrag(l16, ks);
+            fb[ks] = kfrag(16 + l16, ks);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const bf16x8 qb = __builtin_bit_cast(
+                bf16x8, u32x4{rr[4 * ks], rr[4 * ks + 1], rr[4 * ks + 2], rr[4 * ks + 3]});
+            sa[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks % kAhead], qb, sa[ks & 1],
+                                                                 0, 0, 0);
+            sb[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[ks % kAhead], qb, sb[ks & 1],
+                                                                 0, 0, 0);
+            if (ks + kAhead < 16) {
+                fa[ks % kAhead] = kfrag(l16, ks + kAhead);
+                fb[ks % kAhead] = kfrag(16 + l16, ks + kAhead);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);     // DS reads
+#pragma unroll
+        for (int ks = 0; ks < 16 - kAhead; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);            // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // DS reads
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+        const f32x4 s0 = sa[0] + sa[1], s1 = sb[0] + sb[1];
+        // Lane holds the scores of head hc for rows 4lg + r (s0) and 16 + 4lg + r (s1).
+        const uint32_t vm = vmask[t % kMetaTiles];
+        const uint32_t m0 = vm >> (4 * lg), m1 = vm >> (16 + 4 * lg);
+        float xs[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            xs[r] = (m0 >> r) & 1u ? s0[r] * p.qk_scale_log2 : -INFINITY;
+            xs[4 + r] = (m1 >> r) & 1u ? s1[r] * p.qk_scale_log2 : -INFINITY;
+            mx = fmaxf(mx, fmaxf(xs[r], xs[4 + r]));
+        }
+        mx = xrow_max4(mx);
+        // Move the running max only when a score exceeds it by more than the
+        // slack (always on the first valid score).
+        const bool move = mx > m_run + kRescaleSlack;
+        const float m_use = move ? mx : m_run;
+        const float a = move ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;   // 0 if m_run = -inf
+        // exp2(-inf - m) = 0 for finite m; m_use = -inf only while every
+        // score so far is masked, and then every x is -inf too.
+        const float m_sub = m_use == -INFINITY ? 0.f : m_use;
+        float psum = 0.f;
+        bf16x8 pv8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float e = __builtin_amdgcn_exp2f(xs[i] - m_sub);
+            psum += e;
+            pv8[i] = (__bf16)e;
+        }
+        l_run = l_run * a + xrow_sum4(psum);
+        m_run = m_use;
+        // Slots 8lg .. 8lg+7 of the head's row: entries 4lg + r, then 16 + 4lg + r.
+        *reinterpret_cast<bf16x8*>(Pb + (t & 1) * (HG * kPLd) + hc * kPLd + 8 * lg) = pv8;
+        if (lg == 0) alpha_s[(t & 1) * HG + hc] = a;
+        const bool any = __builtin_amdgcn_ballot_w64(move) != 0;
+        if (lane == 0) flags[(t & 1) * 4 + wave] = any ? 1 : 0;
+    };
+
+    // Output scale and lse of the consumer lane's head (lanes of row 0).
     const bool direct = p.S == 1;
-    if (consumer && lg == 0) {
+    auto finish = [&]() __attribute__((always_inline)) {
         const int h = h0 + hc;
         float scale, lse;
         if (direct && p.sink) {
@@ -448,24 +563,44 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         } else {
             p.part_lse[((int64_t)b * p.H + h) * p.S + s] = lse;
         }
-    }
-    __syncthreads();
+    };
 
-    // Output through LDS as bf16 (the final output, or the split's partial):
-    // lane holds O[16mt + 4lg + r][64w + 16nt + l16].
-    constexpr int LD = L::stage_ld;
-    __bf16* st = reinterpret_cast<__bf16*>(smem + L::stage);        // [HG][520]
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&fin[16 * mt + 4 * lg]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                st[(16 * mt + 4 * lg + r) * LD + 64 * wave + 16 * nt + l16] =
-                    (__bf16)(acc[mt][nt][r] * sc[r]);
+    // Pipeline step t = 0..ntiles, then one barrier: QK + softmax of tile t
+    // (consumers), PV of tile t-1 (all waves), dequantisation of tile t+1 and
+    // loads of tile t+3 (producers), staged resolution of the next half
+    // (waves 0..3).  Producers and the other waves run separate loops with
+    // the same barriers, so the producers' loop holds no load but their own
+    // and the compiler counts them exactly: storing tile t+1 waits for its
+    // loads only, with tile t+2's still in flight.  rr[O..O+19] holds tile
+    // t+1's raw bytes and receives tile t+3's (O = 32 for even t, 0 for odd).
+    if (producer) {
+        auto pstep = [&](int t, auto off) __attribute__((always_inline)) {
+            constexpr int O = decltype(off)::value;
+            const PatchSrc a = patch_src(meta_tile(t + 3), prow, t + 3 < ntiles);
+            store_patch<O>(rr, prow, l8, kbuf(t + 1));
+            load_patch<O>(a, l8, rr);
+            if (t >= 1) pv(t - 1);
+            __syncthreads();
+        };
+        for (int t = 0; t <= ntiles; t += 2) {
+            pstep(t, std::integral_constant<int, 32>{});
+            if (t + 1 <= ntiles) pstep(t + 1, std::integral_constant<int, 0>{});
+        }
+    } else {
+        auto cstep = [&](int t) __attribute__((always_inline)) {
+            resolve_stage(t);
+            if (consumer) {
+                if (t < ntiles) qk(t);
+                else if (lg == 0) finish();
+            }
+            if (t >= 1) pv(t - 1);
+            __syncthreads();
+        };
+        for (int t = 0; t <= ntiles; ++t) cstep(t);
     }
-    __syncthreads();
+
+    // Output: 8-byte stores straight from the accumulators (the final bf16
+    // output, or the split's bf16 partial); 4 lanes cover 32 contiguous bytes.
     uint16_t* dst;
     int64_t row_stride;
     if (direct) {
@@ -475,10 +610,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         dst = p.part_o + (((int64_t)b * p.H + h0) * p.S + s) * kD;
         row_stride = (int64_t)p.S * kD;
     }
-    for (int c = tid; c < HG * (kD / 8); c += kThreads) {
-        const int row = c >> 6, col = (c & 63) * 8;
-        *reinterpret_cast<bf16x8*>(dst + row * row_stride + col) =
-            *reinterpret_cast<const bf16x8*>(&st[row * LD + col]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const float sc = fin[16 * mt + l16];
+        uint16_t* row = dst + (16 * mt + l16) * row_stride + 64 * wave + 4 * lg;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (__bf16)(acc[mt][nt][r] * sc);
+            *reinterpret_cast<bf16x4*>(row + 16 * nt) = o;
+        }
     }
 }
 

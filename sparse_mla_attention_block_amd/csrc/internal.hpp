@@ -27,27 +27,29 @@ constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin
 constexpr int kCombineThreads = 128;  // 4 output dims per thread
 
-// LDS tile geometry.  The +8 pad moves consecutive rows onto different banks.
-constexpr int kKnLd = kD + 8;       // row-major K tile [32][520] bf16, double-buffered
-constexpr int kPLd = kTile + 8;     // probabilities    [HG][40] bf16
+// LDS tile geometry.  K tiles are row-major [32][512] bf16 with the 16-byte
+// units of each row permuted (see the kernel); probabilities [HG][40] bf16.
+constexpr int kPLd = kTile + 8;
 constexpr int kMetaTiles = 32;      // resolved-entry ring: two halves of 16 tiles
 
-// LDS carve-up of the partial kernel (bytes).  The epilogue stages the
-// workgroup's whole bf16 output over everything but `fin`.
+// LDS carve-up of the partial kernel (bytes).  K tiles rotate through three
+// buffers (one being written, one read by QK, one read by PV); probabilities,
+// rescale factors and rescale flags through two.
+constexpr int kKBufs = 3;
+
 template <int HG>
 struct Smem {
     static constexpr int fin = 0;                                  // [HG] f32
-    static constexpr int flags = fin + HG * 4;                     // [4] int
-    static constexpr int alpha = flags + 16;                       // [HG] f32
-    static constexpr int pb = alpha + HG * 4;                      // [HG][40] bf16
-    static constexpr int vmask = pb + HG * kPLd * 2;               // [32 tiles] u32
-    static constexpr int kn = vmask + kMetaTiles * 4;              // [2][32][520] bf16
-    static constexpr int meta = kn + 2 * kTile * kKnLd * 2;        // [32 tiles][32][2] int64
-    static constexpr int loop_end = meta + kMetaTiles * kTile * 16;
-    static constexpr int stage = alpha;                            // epilogue staging
-    static constexpr int stage_ld = kD + 8;                        // bf16 per staged row
-    static constexpr int stage_end = stage + HG * stage_ld * 2;
-    static constexpr int bytes = loop_end > stage_end ? loop_end : stage_end;
+    static constexpr int flags = fin + HG * 4;                     // [2][4] int
+    static constexpr int alpha = flags + 32;                       // [2][HG] f32
+    static constexpr int pb = alpha + 2 * HG * 4;                  // [2][HG][40] bf16
+    static constexpr int pb_buf = HG * kPLd * 2;
+    static constexpr int vmask = pb + 2 * pb_buf;                  // [32 tiles] u32
+    static constexpr int kn = vmask + kMetaTiles * 4;              // [3][32][512] bf16
+    static constexpr int kn_buf = kTile * kD * 2;
+    static constexpr int meta = kn + kKBufs * kn_buf;              // [32 tiles][32][2] int64
+    static constexpr int bytes = meta + kMetaTiles * kTile * 16;
+    static_assert(pb % 16 == 0 && kn % 16 == 0 && meta % 16 == 0, "alignment");
     static_assert(bytes <= 160 * 1024, "LDS");
 };
 

@@ -49,8 +49,9 @@ def _desc(B, H, topk, swa, bs=64, num_blocks=1000, **kw):
     return dsv4.make_desc(**d)
 
 
-def _expected_auto_splits(B, H, Kt):
-    groups = -(-H // 64)
+def _expected_splits(B, groups, Kt, forced):
+    if forced:
+        return forced
     if B >= 256:
         return 1
     cap = 4 if Kt <= 1024 else 32
@@ -58,13 +59,25 @@ def _expected_auto_splits(B, H, Kt):
     return max(1, min(want, cap, -(-Kt // 32)))
 
 
+def _expected_plan(B, H, Kt, forced=0):
+    """(heads_per_group, splits): the largest of 64/48/32/16 dividing H whose
+    grid B * S * groups reaches 256 workgroups, else 16."""
+    for hg in (64, 48, 32, 16):
+        if H % hg:
+            continue
+        S = _expected_splits(B, H // hg, Kt, forced)
+        if B * S * (H // hg) >= 256:
+            break
+    return hg, S
+
+
 @pytest.mark.parametrize("ci", range(5))
 def test_plan_of_each_workload(ci):
     c = CONFIGS[ci]
     Kt = c["topk"] + c["swa"]
     p = dsv4.dsv4_sparse_decode_plan(_desc(c["B"], c["H"], c["topk"], c["swa"]), c["num_splits"])
-    S = c["num_splits"] or _expected_auto_splits(c["B"], c["H"], Kt)
-    assert p.num_splits == S
+    hg, S = _expected_plan(c["B"], c["H"], Kt, c["num_splits"])
+    assert (p.heads_per_group, p.num_splits) == (hg, S)
     assert p.heads_per_group * p.head_groups == c["H"]
     assert p.heads_per_group <= 64 and p.heads_per_group % 16 == 0
     units = c["B"] * S
@@ -84,11 +97,26 @@ def test_selector_values_for_the_five_workloads():
     assert got == [1, 4, 32, 1, 4]
 
 
+def test_head_grouping_of_the_five_workloads():
+    got = [dsv4.dsv4_sparse_decode_plan(_desc(c["B"], c["H"], c["topk"], c["swa"]),
+                                        c["num_splits"]).heads_per_group for c in CONFIGS]
+    assert got == [16, 16, 16, 64, 64]
+
+
 @pytest.mark.parametrize("H,hg,groups", [(16, 16, 1), (32, 32, 1), (48, 48, 1), (64, 64, 1),
-                                          (96, 48, 2), (128, 64, 2)])
-def test_head_grouping(H, hg, groups):
-    p = dsv4.dsv4_sparse_decode_plan(_desc(2, H, 100, 0), 1)
+                                          (80, 16, 5), (96, 48, 2), (112, 16, 7), (128, 64, 2)])
+def test_head_grouping_when_the_batch_fills_the_chip(H, hg, groups):
+    p = dsv4.dsv4_sparse_decode_plan(_desc(256, H, 100, 0), 1)
     assert (p.heads_per_group, p.head_groups) == (hg, groups)
+
+
+@pytest.mark.parametrize("H,B,S,hg", [(64, 256, 1, 64), (64, 64, 1, 16), (64, 64, 2, 32),
+                                       (64, 32, 2, 16), (128, 16, 8, 64), (128, 2, 8, 16),
+                                       (96, 2, 4, 16), (96, 64, 2, 48)])
+def test_head_grouping_shrinks_while_cus_would_idle(H, B, S, hg):
+    p = dsv4.dsv4_sparse_decode_plan(_desc(B, H, 1000, 0), S)
+    assert p.heads_per_group == hg == _expected_plan(B, H, 1000, S)[0]
+    assert p.head_groups * p.heads_per_group == H
 
 
 def _status(desc, splits=0):
@@ -111,9 +139,7 @@ def test_validation_errors():
     assert _status(_desc(1, 64, 10, 2, topk_idx_stride=11)) == E
     assert _status(_desc(1, 64, 10, 0), 65) == E
     assert _status(_desc(1, 64, 10, 0), -1) == E
-    N = dsv4.DSV4_ERR_NOT_SUPPORTED
-    assert _status(_desc(1, 80, 10, 0)) == N             # 2 groups of 40
-    assert _status(_desc(1, 112, 10, 0)) == N
+    assert _status(_desc(1, 136, 10, 0)) == E
     assert "num_heads" in dsv4.dsv4_last_error()
 
 

@@ -60,6 +60,19 @@ def test_head_counts(H):
     _check(w, f"H={H} S=1", num_splits=1)
 
 
+@pytest.mark.parametrize("H,hg", [(32, 32), (48, 48), (64, 64), (80, 16), (96, 48), (128, 64)])
+def test_every_head_group_variant(H, hg):
+    """A batch of 256 tokens keeps the largest head group, so each kernel
+    variant (16, 32, 48, 64 heads per workgroup) runs on a full-size grid."""
+    import sparse_mla_attention_block_amd as dsv4
+    rng = np.random.default_rng(40 + H)
+    w = make_custom(B=256, H=H, topk=48, swa=16, seq_lens=list(rng.integers(64, 400, 256)),
+                    seed=40 + H, invalid_frac=0.05, valid_len_range=(20, 48))
+    plan = dsv4.dsv4_sparse_decode_plan(_gh().make_desc(w), 0)
+    assert (plan.heads_per_group, plan.num_splits) == (hg, 1)
+    _check(w, f"H={H} hg={hg}", num_splits=0)
+
+
 @pytest.mark.parametrize("bs,pad", [(1, 0), (1, 8), (16, 0), (64, 64)])
 def test_block_sizes_and_page_strides(bs, pad):
     w = make_custom(B=2, H=64, topk=150, swa=16, seq_lens=[2000, 321], seed=30 + bs + pad,
