@@ -20,7 +20,7 @@
 //     score exceeds it by more than 2^8), writing bf16 probabilities;
 //   * waves 4..7 ("producers", 8 lanes per cache row) dequantise tile t+1
 //     (FP8 x 2^(code-127) -> bf16 in one scaled convert per 2 values) into
-//     one of three LDS K buffers and issue the loads of tile t+3, keeping two
+//     one of three LDS K buffers and issue the loads of tile t+4, keeping three
 //     tiles of raw bytes in flight in registers;
 //   * all 8 waves run PV of tile t-1 on bf16 MFMA, wave w owning output dims
 //     [64w, 64w+64); the V operand comes straight from the K tile through
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // One 64-register array per lane, used by role: consumers keep the q
     // row of their head in it (lane (l16, lg) holds dims 32*ks + 8*lg .. +7
     // of head 16*wave + l16 in rr[4ks..4ks+3], the B operand of QK);
-    // producers keep two tiles of raw bytes in it (rr[0..19], rr[32..51]).
+    // producers keep three tiles of raw bytes in it (rr[0..59]).
     uint32_t rr[64];
     float sink_l2 = -INFINITY;                   // consumer lane's sink, base-2 units
     if (consumer) {
@@ -344,10 +344,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 
     if (producer) {
         load_patch<0>(patch_src(meta_tile(0), prow, ntiles > 0), l8, rr);
-        load_patch<32>(patch_src(meta_tile(1), prow, ntiles > 1), l8, rr);
-        const PatchSrc a2 = patch_src(meta_tile(2), prow, ntiles > 2);
+        load_patch<20>(patch_src(meta_tile(1), prow, ntiles > 1), l8, rr);
+        load_patch<40>(patch_src(meta_tile(2), prow, ntiles > 2), l8, rr);
+        const PatchSrc a3 = patch_src(meta_tile(3), prow, ntiles > 3);
         store_patch<0>(rr, prow, l8, kbuf(0));
-        load_patch<0>(a2, l8, rr);
+        load_patch<0>(a3, l8, rr);
     }
     __syncthreads();
 
@@ -425,9 +426,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // transpose read: lane j of 16-lane group g addresses entry 4g + j/4 (and
     // 16 + 4g + j/4) at dims base + 4(j%4), so lane i receives dim base + i
     // of entries 4g .. 4g+3 (16 + 4g .. 16 + 4g+3).
-    auto pv = [&](int k) __attribute__((always_inline)) {
-        const __bf16* K = kbuf(k);
-        const __bf16* P = Pb + (k & 1) * (HG * kPLd);
+    // Rescale of the accumulators before PV of tile k (rare: only when a
+    // consumer moved its running max in tile k), kept apart from the MFMA
+    // part so the latter sits in one basic block with the consumers' softmax.
+    auto pv_rescale = [&](int k) __attribute__((always_inline)) {
         const int* fl = flags + (k & 1) * 4;
         bool rescale = false;
 #pragma unroll
@@ -441,6 +443,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                 for (int nt = 0; nt < 4; ++nt) acc[mt][nt] *= a;
             }
         }
+    };
+    auto pv_mma = [&](int k) __attribute__((always_inline)) {
+        const __bf16* K = kbuf(k);
+        const __bf16* P = Pb + (k & 1) * (HG * kPLd);
         bf16x8 pa[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -459,9 +465,17 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
                                                                       0, 0, 0);
         }
     };
+    auto pv = [&](int k) __attribute__((always_inline)) {
+        pv_rescale(k);
+        pv_mma(k);
+    };
 
-    // QK + online softmax of tile t (consumer waves).
-    auto qk = [&](int t) __attribute__((always_inline)) {
+    // QK of tile t (consumer waves): the raw scores, lane holding head hc at
+    // rows 4lg + r (first) and 16 + 4lg + r (second).
+    struct Scores {
+        f32x4 s0, s1;
+    };
+    auto qk_scores = [&](int t) __attribute__((always_inline)) -> Scores {
         // S^T = K q^T: A operand = K rows (entries), B operand = q (heads).
         // Four accumulator chains (rows 0-15 / 16-31, even / odd k-steps);
         // K fragments are read four k-steps ahead of their MFMAs, an order
@@ -501,8 +515,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // DS reads
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
-        const f32x4 s0 = sa[0] + sa[1], s1 = sb[0] + sb[1];
-        // Lane holds the scores of head hc for rows 4lg + r (s0) and 16 + 4lg + r (s1).
+        return Scores{sa[0] + sa[1], sb[0] + sb[1]};
+    };
+
+    // Mask + online softmax of tile t (consumer waves), writing P, alpha and
+    // the rescale flag of the tile.
+    auto softmax = [&](int t, const Scores sc) __attribute__((always_inline)) {
+        const f32x4 s0 = sc.s0, s1 = sc.s1;
         const uint32_t vm = vmask[t % kMetaTiles];
         const uint32_t m0 = vm >> (4 * lg), m1 = vm >> (16 + 4 * lg);
         float xs[8];
@@ -565,38 +584,64 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         }
     };
 
+    // Both loops run the same nsteps >= ntiles + 1 steps (a multiple of 3, the
+    // producers' unroll, so their loop body has no branch around a load);
+    // steps past ntiles do nothing but the barrier.
+    const int nsteps = (ntiles + 1 + 2) / 3 * 3;
     // Pipeline step t = 0..ntiles, then one barrier: QK + softmax of tile t
     // (consumers), PV of tile t-1 (all waves), dequantisation of tile t+1 and
-    // loads of tile t+3 (producers), staged resolution of the next half
+    // loads of tile t+4 (producers), staged resolution of the next half
     // (waves 0..3).  Producers and the other waves run separate loops with
     // the same barriers, so the producers' loop holds no load but their own
     // and the compiler counts them exactly: storing tile t+1 waits for its
-    // loads only, with tile t+2's still in flight.  rr[O..O+19] holds tile
-    // t+1's raw bytes and receives tile t+3's (O = 32 for even t, 0 for odd).
+    // loads only, with tiles t+2 and t+3 still in flight.
     if (producer) {
-        auto pstep = [&](int t, auto off) __attribute__((always_inline)) {
-            constexpr int O = decltype(off)::value;
-            const PatchSrc a = patch_src(meta_tile(t + 3), prow, t + 3 < ntiles);
-            store_patch<O>(rr, prow, l8, kbuf(t + 1));
+        // Tile k's raw bytes live in rr[20(k%3) .. +19]; step t stores tile
+        // t+1 into K buffer (t+1)%3 and reuses its registers for tile t+4.
+        auto pstep = [&](int t, auto set) __attribute__((always_inline)) {
+            constexpr int O = 20 * decltype(set)::value;
+            const PatchSrc a = patch_src(meta_tile(t + 4), prow, t + 4 < ntiles);
+            store_patch<O>(rr, prow, l8, Kn + decltype(set)::value * (kTile * kD));
             load_patch<O>(a, l8, rr);
-            if (t >= 1) pv(t - 1);
+            if (t >= 1 && t <= ntiles) pv(t - 1);
             __syncthreads();
         };
-        for (int t = 0; t <= ntiles; t += 2) {
-            pstep(t, std::integral_constant<int, 32>{});
-            if (t + 1 <= ntiles) pstep(t + 1, std::integral_constant<int, 0>{});
+        for (int t = 0; t < nsteps; t += 3) {
+            pstep(t, std::integral_constant<int, 1>{});
+            pstep(t + 1, std::integral_constant<int, 2>{});
+            pstep(t + 2, std::integral_constant<int, 0>{});
         }
-    } else {
-        auto cstep = [&](int t) __attribute__((always_inline)) {
+    } else if (consumer) {
+        // Step 0: QK + softmax of tile 0 (or, with no tile, the finish).
+        resolve_stage(0);
+        if (ntiles > 0)
+            softmax(0, qk_scores(0));
+        else if (lg == 0)
+            finish();
+        __syncthreads();
+        // Steady state: QK of tile t, then PV of tile t-1 (independent of it)
+        // in the same basic block as the softmax of tile t, so the softmax's
+        // VALU work overlaps the PV MFMAs.
+        for (int t = 1; t < ntiles; ++t) {
             resolve_stage(t);
-            if (consumer) {
-                if (t < ntiles) qk(t);
-                else if (lg == 0) finish();
-            }
-            if (t >= 1) pv(t - 1);
+            pv_rescale(t - 1);
+            const Scores sc = qk_scores(t);
+            pv_mma(t - 1);
+            softmax(t, sc);
             __syncthreads();
-        };
-        for (int t = 0; t <= ntiles; ++t) cstep(t);
+        }
+        if (ntiles > 0) {
+            if (lg == 0) finish();
+            pv(ntiles - 1);
+            __syncthreads();
+        }
+        for (int t = ntiles + 1; t < nsteps; ++t) __syncthreads();
+    } else {
+        for (int t = 0; t < nsteps; ++t) {
+            resolve_stage(t);
+            if (t >= 1 && t <= ntiles) pv(t - 1);
+            __syncthreads();
+        }
     }
 
     // Output: 8-byte stores straight from the accumulators (the final bf16
