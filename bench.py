@@ -231,6 +231,15 @@ def main() -> int:
     kt_part = time_graph(capture(lambda r: partial(gslots_all[r]), K), K)
     kt_comb = time_graph(capture(lambda r: combine(), K), K) if S > 1 else 0.0
 
+    # Floors: the partial kernel's own gather (same grid, same row loads over
+    # the same rotating replicas, no arithmetic), and an empty launch (a
+    # 4-byte fill kernel) for the launch cost of a graph node.
+    words = torch.empty(plan.grid_partial * plan.block_partial, dtype=torch.int32, device=dev)
+    kt_gather = time_graph(capture(lambda r: dsv4.dsv4_gather_floor(
+        desc, kv, None, gslots_all[r], None, S, words), K), K)
+    tiny = torch.empty(1, dtype=torch.int32, device=dev)
+    kt_empty = time_graph(capture(lambda r: tiny.fill_(r), K), K)
+
     # Cache-warm reference: one replica, same step.
     g_hot = capture(lambda r: step(0), K)
     hot_ms_per_step = time_graph(g_hot, K)
@@ -270,13 +279,14 @@ def main() -> int:
                         "shuffled pages, 1% invalid, fp8_ds_mla rows, sink, sm_scale 512^-0.5",
             "B": B, "H": H, "topk": w.topk, "swa": w.swa, "block_size": w.block_size,
             "valid_entries": n_valid, "num_splits": S, "grid_partial": plan.grid_partial,
+            "heads_per_group": plan.heads_per_group,
             "replicas": R, "cache_pool_GB": round(R * nb * stride / 1e9, 2),
             "graph_replay": not args.eager, "parallelism": "single GPU",
         },
         "achieved_hbm_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_partial_kernel<64>",
+            "kernel": f"decode_partial_kernel<{plan.heads_per_group}>",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -286,6 +296,8 @@ def main() -> int:
             "mfma_frac": flops / (kt_part * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         },
         "kernels_ms": {"convert": kt_conv, "decode_partial": kt_part, "combine": kt_comb},
+        "floors_ms": {"gather_only": kt_gather, "empty_launch": kt_empty,
+                      "partial_over_gather": kt_part / kt_gather},
         "event_ms_per_step": ev_ms_per_step,
         "cache_warm": {"ms_per_step": hot_ms_per_step, "decode_partial_ms": kt_part_hot,
                        "tokens_per_s": n_valid / (hot_ms_per_step * 1e-3)},

@@ -90,6 +90,8 @@ _lib.dsv4_convert_req_index_to_global.argtypes = [
     _P, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int32,
     ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]
 _lib.dsv4_convert_req_index_to_global.restype = ctypes.c_int
+_lib.dsv4_gather_floor.argtypes = [_DESC, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
+_lib.dsv4_gather_floor.restype = ctypes.c_int
 
 
 class Dsv4Error(RuntimeError):
@@ -189,6 +191,16 @@ def dsv4_convert_req_index_to_global(req_id: Optional[torch.Tensor], num_reqs: i
         _ptr(req_id), num_reqs, _ptr(block_table), bt_stride, max_blocks_per_req,
         _ptr(token_indices), ti_stride, num_tokens, width, block_size, _ptr(cu_seqlens),
         invalid_fill, _ptr(out), _stream(stream)))
+
+
+def dsv4_gather_floor(desc, kv_cache: torch.Tensor, block_table: Optional[torch.Tensor],
+                      topk_idx: torch.Tensor, valid_len: Optional[torch.Tensor], num_splits: int,
+                      words: torch.Tensor, stream=None) -> None:
+    """Gather floor of the partial kernel (include/dsv4_diag.h): same grid, same
+    row loads, no arithmetic; `words` is int32/uint32 [grid_partial * 512]."""
+    _check(_lib.dsv4_gather_floor(ctypes.byref(desc), _ptr(kv_cache), _ptr(block_table),
+                                  _ptr(topk_idx), _ptr(valid_len), num_splits, _ptr(words),
+                                  _stream(stream)))
 
 
 def workspace_split_views(workspace: torch.Tensor, batch: int, num_heads: int,

@@ -11,6 +11,7 @@
 #include <string>
 
 #include "dsv4.h"
+#include "dsv4_diag.h"
 #include "internal.hpp"
 
 namespace {
@@ -258,6 +259,28 @@ int dsv4_sparse_decode(const dsv4_decode_desc* desc, const void* q, const void* 
                        int32_t num_splits, hipStream_t stream) {
     return decode_impl(desc, q, kv_cache, block_table, topk_idx, valid_len, sink, out, lse,
                        num_splits, stream, true);
+}
+
+int dsv4_gather_floor(const dsv4_decode_desc* desc, const void* kv_cache,
+                      const int32_t* block_table, const int32_t* topk_idx,
+                      const int32_t* valid_len, int32_t num_splits, uint32_t* words,
+                      hipStream_t stream) {
+    Shape sh;
+    dsv4_plan plan;
+    int st = make_plan(desc, num_splits, &sh, &plan);
+    if (st) return st;
+    if (!kv_cache || !topk_idx || !words)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "kv_cache, topk_idx and words must not be NULL");
+    if (block_table) {
+        if (desc->max_blocks_per_seq < 1)
+            return fail(DSV4_ERR_INVALID_ARGUMENT, "max_blocks_per_seq must be >= 1 with a block table");
+        if (desc->block_table_stride < desc->max_blocks_per_seq)
+            return fail(DSV4_ERR_INVALID_ARGUMENT, "block_table_stride < max_blocks_per_seq");
+    }
+    const dsv4::DecodeParams p = make_params(desc, sh, nullptr, kv_cache, block_table, topk_idx,
+                                             valid_len, nullptr, nullptr, nullptr);
+    (void)hipGetLastError();
+    return launched(dsv4::launch_gather_floor(p, plan.grid_partial, words, stream), "gather floor");
 }
 
 int dsv4_sparse_decode_partial(const dsv4_decode_desc* desc, const void* q,

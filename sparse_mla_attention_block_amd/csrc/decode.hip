@@ -726,6 +726,77 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
     if (threadIdx.x == 0 && p.lse) p.lse[bh] = lse;
 }
 
+// Gather floor: the partial kernel's work units (same grid, same XCD
+// mapping, same per-split entry range) and the same row loads (8 lanes per
+// row, 9 x 8 data bytes + the 8-byte scale word, rows that take no part read
+// the zero row), with no LDS tile and no arithmetic beyond folding the loaded
+// words into one word per thread.  Resolution of up to 1024 entries goes to
+// LDS first; the loads then run 4 passes of 64 rows deep.  Its duration is
+// the floor the partial kernel's memory traffic sets.
+__global__ __launch_bounds__(kThreads) void gather_floor_kernel(const DecodeParams p,
+                                                                uint32_t* words) {
+    __shared__ int64_t addr[kMetaTiles * kTile][2];
+    const int64_t Lb = blockIdx.x;
+    const int x = (int)(Lb % kXcds);
+    const int64_t r8 = Lb / kXcds;
+    const int64_t unit = (r8 / p.G) * kXcds + x;
+    if (unit >= p.units) return;
+    const int b = (int)(unit / p.S);
+    const int s = (int)(unit % p.S);
+    const int vl = p.valid_len ? min(max(p.valid_len[b], 0), p.topk) : p.topk;
+    const int eff = vl + p.swa;
+    int chunk = (eff + p.S - 1) / p.S;
+    chunk = (chunk + kTile - 1) / kTile * kTile;
+    const int lo = min(s * chunk, eff);
+    const int hi = min(lo + chunk, eff);
+    const int tid = threadIdx.x, row = tid >> 3, l8 = tid & 7;
+    constexpr int kRing = kMetaTiles * kTile;            // 1024 entries
+    uint32_t acc = 0;
+    for (int base = lo; base < hi; base += kRing) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int i = tid + e * kThreads;
+            const int32_t id = load_index(p, b, vl, hi, base + i);
+            const int64_t pg = lookup_page(p, b, id);
+            const uint8_t* pgp = p.kv + pg * p.page_stride;
+            const int64_t off = id % p.bs;
+            addr[i][0] = reinterpret_cast<int64_t>(pg >= 0 ? pgp + off * kRowData : kZeroRow);
+            addr[i][1] = reinterpret_cast<int64_t>(
+                pg >= 0 ? pgp + (int64_t)p.bs * kRowData + off * kRowScale : kZeroRow + kRowData);
+        }
+        __syncthreads();
+        const int n = min(hi - base, kRing);
+        for (int r0 = 0; r0 < n; r0 += 4 * 64) {
+            uint64_t v[4][kChunks + 1];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int r = r0 + 64 * h + row;
+                gbyte* src = (gbyte*)(r < n ? addr[r][0] : reinterpret_cast<int64_t>(kZeroRow));
+                gbyte* sc = (gbyte*)(r < n ? addr[r][1] : reinterpret_cast<int64_t>(kZeroRow));
+#pragma unroll
+                for (int j = 0; j < kChunks; ++j) v[h][j] = *(gu64*)(src + 8 * l8 + 64 * j);
+                v[h][kChunks] = *(gu64*)sc;
+            }
+            // The scale word is loaded by all 8 lanes of a row and folded by one.
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                if (l8 != 0) v[h][kChunks] = 0;
+#pragma unroll
+                for (int j = 0; j <= kChunks; ++j) acc ^= (uint32_t)v[h][j] ^ (uint32_t)(v[h][j] >> 32);
+            }
+        }
+        __syncthreads();
+    }
+    words[Lb * kThreads + tid] = acc;
+}
+
+hipError_t launch_gather_floor(const DecodeParams& p, int64_t grid, uint32_t* words,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(gather_floor_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p,
+                       words);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
                                  hipStream_t stream) {
     const dim3 g((unsigned)grid), blk(kThreads);

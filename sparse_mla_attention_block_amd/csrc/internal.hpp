@@ -105,5 +105,7 @@ hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int
                                  hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
+hipError_t launch_gather_floor(const DecodeParams& p, int64_t grid, uint32_t* words,
+                               hipStream_t stream);
 
 }  // namespace dsv4

@@ -15,16 +15,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_symbols():
-    text = open(os.path.join(ROOT, "include", "dsv4.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsv4_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(dsv4_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = _declared_symbols()
     for want in ("dsv4_sparse_decode", "dsv4_sparse_decode_partial", "dsv4_combine_splits",
                  "dsv4_convert_req_index_to_global", "dsv4_sparse_decode_plan",
-                 "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error"):
+                 "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error",
+                 "dsv4_gather_floor"):
         assert want in names
 
 

@@ -225,3 +225,40 @@ def test_side_stream_and_no_overrun():
     ro, rl = _ref(w)
     gh.assert_decode_close(out.float().double().cpu().numpy(), lse.double().cpu().numpy(), ro,
                            rl, "side stream")
+
+
+def test_gather_floor_loads_exactly_the_taking_part_rows():
+    """The gather floor folds every word of every taking-part row once per head
+    group; with one head group the XOR over all its output words equals the
+    XOR of those rows' 576 data bytes and 8 scale bytes, read on the host."""
+    import sparse_mla_attention_block_amd as dsv4
+    gh = _gh()
+    w = make_custom(B=3, H=16, topk=300, swa=20, seq_lens=[4000, 900, 64], seed=61,
+                    invalid_frac=0.1, valid_len_range=(100, 300))
+    dw = gh.DeviceWorkload(w)
+    desc = gh.make_desc(w)
+    plan = dsv4.dsv4_sparse_decode_plan(desc, 3)
+    assert plan.head_groups == 1
+    words = torch.full((plan.grid_partial * plan.block_partial,), -1, dtype=torch.int32,
+                       device="cuda")
+    print("gather floor: B=3 H=16 S=3", flush=True)
+    dsv4.dsv4_gather_floor(desc, dw.kv, dw.bt, dw.idx, dw.vl, 3, words)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(words.cpu().numpy().view(np.uint32))
+    want = np.uint32(0)
+    kv = w.kv
+    for b in range(w.B):
+        vl = min(max(int(w.valid_len[b]), 0), w.topk)
+        cols = list(range(vl)) + list(range(w.topk, w.topk + w.swa))
+        for c in cols:
+            i = int(w.topk_idx[b, c])
+            if i < 0 or i // w.block_size >= w.max_blocks_per_seq:
+                continue
+            pg = int(w.block_table[b, i // w.block_size])
+            if pg < 0 or pg >= w.num_blocks:
+                continue
+            off = i % w.block_size
+            data = kv[pg, off * 576:(off + 1) * 576]
+            sc = kv[pg, w.block_size * 576 + off * 8: w.block_size * 576 + off * 8 + 8]
+            want ^= np.bitwise_xor.reduce(np.concatenate([data, sc]).view(np.uint32))
+    assert got == want
