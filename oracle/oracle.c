@@ -105,7 +105,12 @@ int orc_resolve(const orc_desc* d, const int32_t* block_table, int32_t b, int32_
 /* Row bytes at page*stride + off*576; its 8 scale bytes at
  * page*stride + block_size*576 + off*8.  NoPE dim j = E4M3FN(byte j) times
  * UE8M0(code j/64); RoPE dim r = bf16 from bytes 448+2r (low) and 449+2r.
- * [SGL-26208] DSV4 constants and the gather+dequant address arithmetic. */
+ * [SGL-26208] DSV4 constants and the gather+dequant address arithmetic.
+ * With d->scrub, a dimension whose value is not finite (an FP8 NaN byte, a
+ * NaN scale code, a NaN or infinite RoPE value) is read as 0: the legacy
+ * element-wise clearing the decode keeps when the cache is not trusted to
+ * be NaN-free ([vLLM-52212] implementation item 3 and the provenance gate
+ * in its ROCm entry-layer snippet). */
 void orc_dequant_row(const orc_desc* d, const uint8_t* kv, int64_t page, int32_t off,
                      double* out) {
     const uint8_t* data = kv + page * d->page_stride + (int64_t)off * ORC_ROW_DATA;
@@ -117,6 +122,9 @@ void orc_dequant_row(const orc_desc* d, const uint8_t* kv, int64_t page, int32_t
         uint16_t bits = (uint16_t)(data[ORC_DNOPE + 2 * r] | (data[ORC_DNOPE + 2 * r + 1] << 8));
         out[ORC_DNOPE + r] = orc_bf16(bits);
     }
+    if (d->scrub)
+        for (j = 0; j < ORC_D; ++j)
+            if (!isfinite(out[j])) out[j] = 0.0;
 }
 
 /* valid_len clamps to [0, topk]; NULL means the whole main list. */

@@ -31,6 +31,8 @@ typedef struct {
     int64_t block_table_stride;  /* elements between block-table rows        */
     int64_t page_stride;         /* bytes between pages                      */
     double sm_scale;             /* softmax scale on q.k (not on the sink)   */
+    int32_t scrub;               /* 1: every dequantised element that is not
+                                    finite is read as 0 (decode-time scrub)  */
 } orc_desc;
 
 /* Scalar decoders. */

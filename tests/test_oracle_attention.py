@@ -260,3 +260,52 @@ def test_poison_rows_are_never_read():
     o2, l2, _ = oracle.decode_workload(w, topk_idx=ti)
     assert np.all(np.isfinite(o2))
     assert np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
+def _poisoned_and_cleaned(w, seed):
+    """Plant non-finite values in taking-part rows of token 0: FP8 NaN bytes in
+    the NoPE part, a NaN scale code (255) on one group, a NaN and an infinite
+    RoPE value.  Returns (poisoned kv, cleaned kv) where the cleaned pool holds
+    a finite 0 wherever the poisoned one dequantises to a non-finite value."""
+    rng = np.random.default_rng(seed)
+    kv_p, kv_c = w.kv.copy(), w.kv.copy()
+    bs = w.block_size
+    m = _entry_mask(w, 0)
+    slots = [int(w.topk_idx[0, k]) for k in np.flatnonzero(m)][:4]
+    for i, slot in enumerate(slots):
+        pg, off = int(w.block_table[0, slot // bs]), slot % bs
+        data = off * 576
+        scale = bs * 576 + off * 8
+        nan_bytes = rng.choice(448, size=5, replace=False)
+        kv_p[pg, data + nan_bytes] = np.where(rng.random(5) < 0.5, 0x7F, 0xFF)
+        kv_c[pg, data + nan_bytes] = 0
+        if i == 0:                                   # NaN scale on group 3
+            kv_p[pg, scale + 3] = 255
+            kv_c[pg, scale + 3] = 127
+            kv_c[pg, data + 192:data + 256] = 0
+        r = int(rng.integers(0, 63))
+        kv_p[pg, data + 448 + 2 * r:data + 450 + 2 * r] = [0xC0, 0x7F]      # bf16 NaN
+        kv_p[pg, data + 450 + 2 * r:data + 452 + 2 * r] = [0x80, 0xFF]      # bf16 -inf
+        kv_c[pg, data + 448 + 2 * r:data + 452 + 2 * r] = 0
+    return kv_p, kv_c
+
+
+def test_scrub_is_the_identity_on_a_finite_cache():
+    w = _w(111)
+    out, lse, _ = oracle.decode_workload(w)
+    o2, l2, _ = oracle.decode_workload(w, scrub=True)
+    assert np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
+@pytest.mark.parametrize("S", [0, 3])
+def test_scrub_reads_non_finite_elements_as_zero(S):
+    """Scrubbing a poisoned pool gives exactly what the same pool with those
+    elements set to a finite 0 gives without scrubbing; unscrubbed, the poison
+    reaches token 0's output."""
+    w = _w(112, B=2, seq_lens=[700, 300])
+    kv_p, kv_c = _poisoned_and_cleaned(w, 5)
+    o_s, l_s, _ = oracle.decode_workload(w, kv=kv_p, scrub=True, num_splits=S)
+    o_c, l_c, _ = oracle.decode_workload(w, kv=kv_c, num_splits=S)
+    assert np.all(np.isfinite(o_s)) and np.array_equal(o_s, o_c) and np.array_equal(l_s, l_c)
+    o_u, _, _ = oracle.decode_workload(w, kv=kv_p, num_splits=S)
+    assert np.isnan(o_u[0]).any() and np.array_equal(o_u[1], o_c[1])

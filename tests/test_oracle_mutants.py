@@ -47,6 +47,9 @@ MUTANTS = {
                                "int64_t g = page * block_size;"),
     "convert_no_block_check": ("if (blk < max_blocks_per_req) {", "if (1) {"),
     "convert_ragged_dense_base": ("base = cu_seqlens[t];", "base = (int64_t)t * width;"),
+    "scrub_nope_only": ("for (j = 0; j < ORC_D; ++j)\n            if (!isfinite(out[j])) out[j] = 0.0;",
+                        "for (j = 0; j < ORC_DNOPE; ++j)\n            if (!isfinite(out[j])) out[j] = 0.0;"),
+    "scrub_ignored": ("if (d->scrub)\n", "if (0)\n"),
     "dot_skips_rope": ("for (j = 0; j < ORC_D; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];",
                        "for (j = 0; j < 448; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];"),
 }
