@@ -59,6 +59,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to defeat the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scrub", action="store_true",
+                    help="decode with the scrub flag (non-finite cache elements read as 0)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a graph "
@@ -129,13 +131,15 @@ def main() -> int:
     out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
 
+    flags = dsv4.DSV4_DECODE_SCRUB if args.scrub else 0
     desc = dsv4.make_desc(batch=B, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
-                          num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale)
+                          num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale, flags=flags)
     plan = dsv4.dsv4_sparse_decode_plan(desc, 0)
     S = plan.num_splits
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
     desc = dsv4.make_desc(batch=B, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
-                          num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale, workspace=ws)
+                          num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale, workspace=ws,
+                          flags=flags)
     part_o, part_l = dsv4.workspace_split_views(ws, B, H, S) if S > 1 else (None, None)
     kv = pool.view(-1)
 
@@ -259,7 +263,7 @@ def main() -> int:
     tokens_per_s = n_valid / (ms_per_step * 1e-3)
     achieved = part_bytes / (kt_part * 1e-3) / 1e9
     digest = _source_digest()
-    traffic = _traffic_from_profile(digest)
+    traffic = None if args.scrub else _traffic_from_profile(digest)
 
     rec = {
         "metric": METRIC,
@@ -279,14 +283,15 @@ def main() -> int:
                         "shuffled pages, 1% invalid, fp8_ds_mla rows, sink, sm_scale 512^-0.5",
             "B": B, "H": H, "topk": w.topk, "swa": w.swa, "block_size": w.block_size,
             "valid_entries": n_valid, "num_splits": S, "grid_partial": plan.grid_partial,
-            "heads_per_group": plan.heads_per_group,
+            "heads_per_group": plan.heads_per_group, "scrub": bool(args.scrub),
             "replicas": R, "cache_pool_GB": round(R * nb * stride / 1e9, 2),
             "graph_replay": not args.eager, "parallelism": "single GPU",
         },
         "achieved_hbm_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"decode_partial_kernel<{plan.heads_per_group}>",
+            "kernel": f"decode_partial_kernel<{plan.heads_per_group}, "
+                      f"{'true' if args.scrub else 'false'}>",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -72,6 +72,18 @@ const char* dsv4_last_error(void);
 
 /* ------------------------------------------------------------ decode */
 
+/* Decode flags (dsv4_decode_desc.flags).
+ *
+ * DSV4_DECODE_SCRUB: every dequantised K/V element that is not finite (an
+ * FP8 NaN byte, scale code 255, a product beyond the bf16 range, a NaN or
+ * infinite RoPE value) is read as 0 before it enters any product.  For a
+ * cache whose writer is not known to keep it NaN-free; a cache whose writer
+ * sanitises non-finite values runs without it, at no cost.  (vLLM PR #52212 page, implementation item 3: element-wise
+ * clearing of NoPE/RoPE is the legacy behaviour, dropped when the cache's
+ * provenance guarantees finite values; its ROCm entry-layer snippet gates
+ * the choice on a flag.)  Other bits are reserved and must be 0. */
+#define DSV4_DECODE_SCRUB 0x1u
+
 typedef struct dsv4_decode_desc {
     int32_t batch;               /* B: query tokens, one per sequence (s_q = 1), >= 1 */
     int32_t num_heads;           /* H: multiple of 16 in [16, 128]                   */
@@ -84,6 +96,7 @@ typedef struct dsv4_decode_desc {
     int64_t page_stride;         /* bytes between pages: >= block_size*584, mult. of 8 */
     int64_t topk_idx_stride;     /* elements between topk_idx rows; 0 = topk + swa   */
     float sm_scale;              /* multiplies q.k (never the sink)                  */
+    uint32_t flags;              /* DSV4_DECODE_* bits; 0 = none                     */
     void* workspace;             /* device scratch for split partials (may be NULL
                                     when the call needs none)                        */
     size_t workspace_bytes;      /* its size                                         */

@@ -31,6 +31,7 @@ DSV4_ERR_NOT_SUPPORTED = 2
 DSV4_ERR_WORKSPACE_TOO_SMALL = 3
 DSV4_ERR_HIP = 4
 MAX_SPLITS = 64
+DSV4_DECODE_SCRUB = 0x1
 
 
 class dsv4_decode_desc(ctypes.Structure):
@@ -46,6 +47,7 @@ class dsv4_decode_desc(ctypes.Structure):
         ("page_stride", ctypes.c_int64),
         ("topk_idx_stride", ctypes.c_int64),
         ("sm_scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -130,13 +132,14 @@ def _stream(stream) -> ctypes.c_void_p:
 def make_desc(*, batch: int, num_heads: int, topk: int, swa: int, block_size: int,
               num_blocks: int, page_stride: int, sm_scale: float, max_blocks_per_seq: int = 0,
               block_table_stride: int = 0, topk_idx_stride: int = 0,
-              workspace: Optional[torch.Tensor] = None) -> dsv4_decode_desc:
+              workspace: Optional[torch.Tensor] = None, flags: int = 0) -> dsv4_decode_desc:
     d = dsv4_decode_desc()
     d.batch, d.num_heads, d.topk, d.swa = batch, num_heads, topk, swa
     d.block_size, d.max_blocks_per_seq = block_size, max_blocks_per_seq
     d.num_blocks, d.block_table_stride, d.page_stride = num_blocks, block_table_stride, page_stride
     d.topk_idx_stride = topk_idx_stride
     d.sm_scale = sm_scale
+    d.flags = flags
     if workspace is not None:
         d.workspace = workspace.data_ptr()
         d.workspace_bytes = workspace.numel() * workspace.element_size()

@@ -70,6 +70,9 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
                     (long long)d->block_size * kRowBytes, (long long)d->page_stride);
     if (d->num_blocks > INT64_MAX / d->page_stride)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "num_blocks * page_stride overflows");
+    if (d->flags & ~DSV4_DECODE_SCRUB)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "unknown decode flags 0x%x",
+                    (unsigned)(d->flags & ~DSV4_DECODE_SCRUB));
     const int64_t idx_stride = d->topk_idx_stride == 0 ? kt : d->topk_idx_stride;
     if (idx_stride < kt)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "topk_idx_stride %lld < topk + swa %lld",
@@ -207,7 +210,9 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
     if (st) return st;
     const dsv4::DecodeParams p = make_params(d, sh, q, kv, bt, idx, valid_len, sink, out, lse);
     (void)hipGetLastError();   // start from a clean error state
-    st = launched(dsv4::launch_decode_partial(p, sh.hg, plan.grid_partial, stream), "decode partial");
+    st = launched(dsv4::launch_decode_partial(p, sh.hg, plan.grid_partial,
+                                                          (d->flags & DSV4_DECODE_SCRUB) != 0,
+                                                          stream), "decode partial");
     if (st || !with_combine || sh.splits == 1) return st;
     dsv4::CombineParams c;
     c.part_o = p.part_o;

@@ -176,20 +176,40 @@ __device__ __forceinline__ void load_patch(PatchSrc a, int l8, uint32_t (&rr)[64
     rr[O + 19] = (uint32_t)(sw >> 32);
 }
 
-// Dequantises the chunks into the K tile.
-template <int O>
+// Two bf16 with any NaN or infinite half replaced by +0.  A half is not
+// finite when its magnitude bits are >= 0x7F80 (all exponent bits set);
+// adding 0x80 to the magnitude then sets bit 15 of that half, with no carry
+// into the other half, and an arithmetic shift by 15 spreads bit 15 into a
+// half-wide mask.
+__device__ __forceinline__ uint32_t scrub_pair(uint32_t w) {
+    typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t t = (w & 0x7FFF7FFFu) + 0x00800080u;
+    const uint32_t bad = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, t) >> (int16_t)15);
+    return w & ~bad;
+}
+
+// Dequantises the chunks into the K tile.  With SCRUB every element that is
+// not finite after dequantisation (an FP8 NaN byte, a NaN scale code, a
+// product past the bf16 range, a NaN or infinite RoPE value) is stored as 0.
+template <int O, bool SCRUB>
 __device__ __forceinline__ void store_patch(const uint32_t (&rr)[64], int prow, int l8,
                                             __bf16* Kt) {
     const uint64_t sw = (uint64_t)rr[O + 19] << 32 | rr[O + 18];
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
         const uint2 raw = make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]);
-        *reinterpret_cast<bf16x8*>(Kt + kofs(prow, 64 * j + 8 * l8)) =
-            dequant8(raw, (uint32_t)(sw >> (8 * j)) & 0xFFu);
+        bf16x8 v = dequant8(raw, (uint32_t)(sw >> (8 * j)) & 0xFFu);
+        if (SCRUB) {
+            u32x4 w = __builtin_bit_cast(u32x4, v);
+            w = u32x4{scrub_pair(w[0]), scrub_pair(w[1]), scrub_pair(w[2]), scrub_pair(w[3])};
+            v = __builtin_bit_cast(bf16x8, w);
+        }
+        *reinterpret_cast<bf16x8*>(Kt + kofs(prow, 64 * j + 8 * l8)) = v;
     }
 #pragma unroll
     for (int j = 7; j < kChunks; ++j) {
-        const uint2 raw = make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]);
+        uint2 raw = make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]);
+        if (SCRUB) raw = make_uint2(scrub_pair(raw.x), scrub_pair(raw.y));
         *reinterpret_cast<uint2*>(Kt + kofs(prow, kDNope + 32 * (j - 7) + 4 * l8)) = raw;
     }
 }
@@ -251,7 +271,7 @@ __device__ __forceinline__ float xrow_sum4(float v) {
     return xrow4(v, [](float p, float q) { return p + q; });
 }
 
-template <int HG>
+template <int HG, bool SCRUB>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
     constexpr int MT = HG / 16;              // 16-head MFMA tiles; consumer wave w owns tile w
     static_assert(HG % 16 == 0 && HG <= kMaxHeadsPerGroup, "head group");
@@ -347,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         load_patch<20>(patch_src(meta_tile(1), prow, ntiles > 1), l8, rr);
         load_patch<40>(patch_src(meta_tile(2), prow, ntiles > 2), l8, rr);
         const PatchSrc a3 = patch_src(meta_tile(3), prow, ntiles > 3);
-        store_patch<0>(rr, prow, l8, kbuf(0));
+        store_patch<0, SCRUB>(rr, prow, l8, kbuf(0));
         load_patch<0>(a3, l8, rr);
     }
     __syncthreads();
@@ -488,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         auto kfrag = [&](int row, int ks) {
             return *reinterpret_cast<const bf16x8*>(K + kofs(row, 32 * ks + 8 * lg));
         };
-        constexpr int kAhead = 4;
+        constexpr int kAhead = 6;
         bf16x8 fa[kAhead], fb[kAhead];
 #pragma unroll
         for (int ks = 0; ks < kAhead; ++ks) {
@@ -601,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         auto pstep = [&](int t, auto set) __attribute__((always_inline)) {
             constexpr int O = 20 * decltype(set)::value;
             const PatchSrc a = patch_src(meta_tile(t + 4), prow, t + 4 < ntiles);
-            store_patch<O>(rr, prow, l8, Kn + decltype(set)::value * (kTile * kD));
+            store_patch<O, SCRUB>(rr, prow, l8, Kn + decltype(set)::value * (kTile * kD));
             load_patch<O>(a, l8, rr);
             if (t >= 1 && t <= ntiles) pv(t - 1);
             __syncthreads();
@@ -797,17 +817,25 @@ hipError_t launch_gather_floor(const DecodeParams& p, int64_t grid, uint32_t* wo
     return hipGetLastError();
 }
 
-hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
-                                 hipStream_t stream) {
-    const dim3 g((unsigned)grid), blk(kThreads);
+template <bool SCRUB>
+static hipError_t launch_partial_variant(const DecodeParams& p, int heads_per_group,
+                                         dim3 g, hipStream_t stream) {
+    const dim3 blk(kThreads);
     switch (heads_per_group) {
-        case 16: hipLaunchKernelGGL(decode_partial_kernel<16>, g, blk, 0, stream, p); break;
-        case 32: hipLaunchKernelGGL(decode_partial_kernel<32>, g, blk, 0, stream, p); break;
-        case 48: hipLaunchKernelGGL(decode_partial_kernel<48>, g, blk, 0, stream, p); break;
-        case 64: hipLaunchKernelGGL(decode_partial_kernel<64>, g, blk, 0, stream, p); break;
+        case 16: hipLaunchKernelGGL((decode_partial_kernel<16, SCRUB>), g, blk, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((decode_partial_kernel<32, SCRUB>), g, blk, 0, stream, p); break;
+        case 48: hipLaunchKernelGGL((decode_partial_kernel<48, SCRUB>), g, blk, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((decode_partial_kernel<64, SCRUB>), g, blk, 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
+                                 bool scrub, hipStream_t stream) {
+    const dim3 g((unsigned)grid);
+    return scrub ? launch_partial_variant<true>(p, heads_per_group, g, stream)
+                 : launch_partial_variant<false>(p, heads_per_group, g, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {

@@ -102,7 +102,7 @@ struct ConvertParams {
 
 // Kernel launchers (return the launch's hipError_t).
 hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
-                                 hipStream_t stream);
+                                 bool scrub, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
 hipError_t launch_gather_floor(const DecodeParams& p, int64_t grid, uint32_t* words,

@@ -17,5 +17,6 @@ from .workloads import (  # noqa: F401
     Workload,
     make_workload,
     make_custom,
+    poison_rows,
     workload_digest,
 )

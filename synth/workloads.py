@@ -276,3 +276,32 @@ def make_convert_case(*, seed: int, num_tokens: int, width: int, block_size: int
         cu[1:] = np.cumsum(n)
     return ConvertCase(req_id=req, block_table=bt, max_blocks=max_blocks, token_indices=ti,
                        width=width, block_size=block_size, cu_seqlens=cu)
+
+
+def poison_rows(w: Workload, b: int, slots: Sequence[int], seed: int, base=None):
+    """Plants non-finite encodings in the cache rows of token ``b``'s
+    request-local ``slots``: five FP8 NaN bytes (0x7F or 0xFF) in the NoPE
+    part of each row, a NaN scale code (255) on group 3 of the first row, and
+    a bf16 NaN then a bf16 -inf at a random RoPE position of each row.
+    Returns (poisoned pool, cleaned pool): the cleaned pool holds, at each
+    planted element, the encoding of a finite zero (byte 0; for the NaN scale
+    group all 64 bytes 0 and code 127).  ``base`` = an earlier (poisoned,
+    cleaned) pair to add to instead of ``w.kv``."""
+    rng = np.random.default_rng(seed)
+    kv_p, kv_c = (w.kv.copy(), w.kv.copy()) if base is None else (base[0].copy(), base[1].copy())
+    bs = w.block_size
+    for i, slot in enumerate(slots):
+        pg, off = int(w.block_table[b, slot // bs]), slot % bs
+        data = off * ROW_DATA_BYTES
+        scale = bs * ROW_DATA_BYTES + off * ROW_SCALE_BYTES
+        nan_bytes = rng.choice(D_NOPE, size=5, replace=False)
+        kv_p[pg, data + nan_bytes] = np.where(rng.random(5) < 0.5, 0x7F, 0xFF)
+        kv_c[pg, data + nan_bytes] = 0
+        if i == 0:
+            kv_p[pg, scale + 3] = 255
+            kv_c[pg, scale + 3] = 127
+            kv_c[pg, data + 192:data + 256] = 0
+        r = D_NOPE + 2 * int(rng.integers(0, D_ROPE - 1))
+        kv_p[pg, data + r:data + r + 4] = [0xC0, 0x7F, 0x80, 0xFF]   # bf16 NaN, bf16 -inf
+        kv_c[pg, data + r:data + r + 4] = 0
+    return kv_p, kv_c

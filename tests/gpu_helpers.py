@@ -38,25 +38,26 @@ class DeviceWorkload:
 _KEEP = object()
 
 
-def make_desc(w, *, use_bt=True, workspace=None):
+def make_desc(w, *, use_bt=True, workspace=None, flags=0):
     return dsv4.make_desc(batch=w.B, num_heads=w.H, topk=w.topk, swa=w.swa,
                           block_size=w.block_size, num_blocks=w.num_blocks,
                           page_stride=w.page_stride, sm_scale=w.sm_scale,
                           max_blocks_per_seq=w.max_blocks_per_seq if use_bt else 0,
                           block_table_stride=w.block_table.shape[1] if use_bt else 0,
-                          workspace=workspace)
+                          workspace=workspace, flags=flags)
 
 
 def gpu_decode(dw: DeviceWorkload, *, num_splits=None, use_bt=True, topk_idx=None,
                valid_len=_KEEP, sink=_KEEP, partial_then_combine=False, stream=None,
-               want_lse=True):
+               want_lse=True, kv=None, flags=0):
     """Runs the decode; returns (out, lse) as float64 numpy arrays."""
     w = dw.w
     S = w.num_splits if num_splits is None else num_splits
-    desc = make_desc(w, use_bt=use_bt)
+    desc = make_desc(w, use_bt=use_bt, flags=flags)
     nbytes = dsv4.dsv4_sparse_decode_workspace_bytes(desc, S)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda") if nbytes else None
-    desc = make_desc(w, use_bt=use_bt, workspace=ws)
+    desc = make_desc(w, use_bt=use_bt, workspace=ws, flags=flags)
+    kv = dw.kv if kv is None else kv
     out = torch.full((w.B, w.H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((w.B, w.H), float("nan"), dtype=torch.float32, device="cuda")
     idx = dw.idx if topk_idx is None else topk_idx
@@ -65,14 +66,14 @@ def gpu_decode(dw: DeviceWorkload, *, num_splits=None, use_bt=True, topk_idx=Non
     bt = dw.bt if use_bt else None
     if partial_then_combine:
         plan = dsv4.dsv4_sparse_decode_plan(desc, S)
-        dsv4.dsv4_sparse_decode_partial(desc, dw.q, dw.kv, bt, idx, vl, sk, out,
+        dsv4.dsv4_sparse_decode_partial(desc, dw.q, kv, bt, idx, vl, sk, out,
                                         lse if want_lse else None, S, stream)
         if plan.num_splits > 1:
             po, pl = dsv4.workspace_split_views(ws, w.B, w.H, plan.num_splits)
             dsv4.dsv4_combine_splits(w.B, w.H, plan.num_splits, po, pl, sk, out,
                                      lse if want_lse else None, stream)
     else:
-        dsv4.dsv4_sparse_decode(desc, dw.q, dw.kv, bt, idx, vl, sk, out,
+        dsv4.dsv4_sparse_decode(desc, dw.q, kv, bt, idx, vl, sk, out,
                                 lse if want_lse else None, S, stream)
     torch.cuda.synchronize()
     return out.float().double().cpu().numpy(), lse.double().cpu().numpy()

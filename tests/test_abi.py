@@ -5,6 +5,7 @@ says, and rejects bad arguments with the documented status codes."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -44,6 +45,32 @@ def test_library_is_built_for_gfx950_only():
     assert b"gfx950" in data
     for other in (b"gfx942", b"gfx90a", b"gfx1100"):
         assert other not in data
+
+
+@pytest.mark.parametrize("struct", ["dsv4_decode_desc", "dsv4_plan"])
+def test_binding_structs_match_the_c_layout(struct, tmp_path):
+    """Every field of the Python mirror sits at the offset a C compiler gives
+    it in include/dsv4.h, and the sizes agree."""
+    cls = getattr(dsv4, struct)
+    fields = [f for f, _ in cls._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"dsv4.h\"\n"
+                   "int main(void) {\n"
+                   + "".join(f'    printf("%zu\\n", offsetof({struct}, {f}));\n' for f in fields)
+                   + f'    printf("%zu\\n", sizeof({struct}));\n    return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [getattr(cls, f).offset for f in fields] + [ctypes.sizeof(cls)]
+    assert got == want
+
+
+def test_unknown_decode_flags_are_rejected():
+    dsv4.dsv4_sparse_decode_plan(_desc(1, 64, 10, 0, flags=dsv4.DSV4_DECODE_SCRUB))
+    assert _status(_desc(1, 64, 10, 0, flags=0x2)) == dsv4.DSV4_ERR_INVALID_ARGUMENT
+    assert "flags" in dsv4.dsv4_last_error()
 
 
 def _desc(B, H, topk, swa, bs=64, num_blocks=1000, **kw):

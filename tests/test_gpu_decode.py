@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from synth import make_custom, make_workload
+from synth import make_custom, make_workload, poison_rows
+import sparse_mla_attention_block_amd as dsv4
 
 pytestmark = pytest.mark.gpu
 
@@ -162,6 +163,38 @@ def test_poisoned_rows_are_never_read_bitwise():
                 ti[b, k] = free.pop() if k % 3 else w.max_blocks_per_seq * w.block_size + k
         dirty = gh.gpu_decode(dw, num_splits=S, topk_idx=torch.from_numpy(ti).cuda())
         assert np.array_equal(clean[0], dirty[0]) and np.array_equal(clean[1], dirty[1])
+
+
+def _used_slots(w, b, n):
+    vl = w.topk if w.valid_len is None else int(w.valid_len[b])
+    return [int(x) for x in w.topk_idx[b, :vl] if x >= 0][:n]
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_scrub_reads_non_finite_elements_as_zero(S):
+    """With the scrub flag, a pool holding FP8 NaN bytes, a NaN scale code and
+    NaN/-inf RoPE values in taking-part rows gives bit for bit what the pool
+    with those elements encoded as finite zeros gives without it, and
+    matches the oracle's scrub mode."""
+    gh = _gh()
+    w = make_custom(B=3, H=64, topk=256, swa=64, seq_lens=[5000, 700, 3000], seed=130,
+                    invalid_frac=0.03, valid_len_range=(150, 256))
+    pair = None
+    for b in range(w.B):
+        pair = poison_rows(w, b, _used_slots(w, b, 6), seed=131 + b, base=pair)
+    kv_p, kv_c = pair
+    w.kv = kv_c
+    dw = gh.DeviceWorkload(w)
+    kv_pd = torch.from_numpy(kv_p).cuda()
+    print(f"scrub S={S}", flush=True)
+    clean = gh.gpu_decode(dw, num_splits=S)
+    scrubbed = gh.gpu_decode(dw, num_splits=S, kv=kv_pd, flags=dsv4.DSV4_DECODE_SCRUB)
+    assert np.array_equal(clean[0], scrubbed[0]) and np.array_equal(clean[1], scrubbed[1])
+    also = gh.gpu_decode(dw, num_splits=S, flags=dsv4.DSV4_DECODE_SCRUB)
+    assert np.array_equal(clean[0], also[0]) and np.array_equal(clean[1], also[1])
+    w.kv = kv_p
+    ro, rl, _ = oracle.decode_workload(w, num_splits=S, scrub=True)
+    gh.assert_decode_close(scrubbed[0], scrubbed[1], ro, rl, "scrub vs oracle")
 
 
 def test_deterministic_bitwise():

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from synth import make_custom
+from synth import make_custom, poison_rows
 
 RTOL = 1e-10
 ATOL = 1e-12
@@ -262,33 +262,12 @@ def test_poison_rows_are_never_read():
     assert np.array_equal(o2, out) and np.array_equal(l2, lse)
 
 
+
 def _poisoned_and_cleaned(w, seed):
-    """Plant non-finite values in taking-part rows of token 0: FP8 NaN bytes in
-    the NoPE part, a NaN scale code (255) on one group, a NaN and an infinite
-    RoPE value.  Returns (poisoned kv, cleaned kv) where the cleaned pool holds
-    a finite 0 wherever the poisoned one dequantises to a non-finite value."""
-    rng = np.random.default_rng(seed)
-    kv_p, kv_c = w.kv.copy(), w.kv.copy()
-    bs = w.block_size
+    """Poison four taking-part rows of token 0 (see synth.poison_rows)."""
     m = _entry_mask(w, 0)
     slots = [int(w.topk_idx[0, k]) for k in np.flatnonzero(m)][:4]
-    for i, slot in enumerate(slots):
-        pg, off = int(w.block_table[0, slot // bs]), slot % bs
-        data = off * 576
-        scale = bs * 576 + off * 8
-        nan_bytes = rng.choice(448, size=5, replace=False)
-        kv_p[pg, data + nan_bytes] = np.where(rng.random(5) < 0.5, 0x7F, 0xFF)
-        kv_c[pg, data + nan_bytes] = 0
-        if i == 0:                                   # NaN scale on group 3
-            kv_p[pg, scale + 3] = 255
-            kv_c[pg, scale + 3] = 127
-            kv_c[pg, data + 192:data + 256] = 0
-        r = int(rng.integers(0, 63))
-        kv_p[pg, data + 448 + 2 * r:data + 450 + 2 * r] = [0xC0, 0x7F]      # bf16 NaN
-        kv_p[pg, data + 450 + 2 * r:data + 452 + 2 * r] = [0x80, 0xFF]      # bf16 -inf
-        kv_c[pg, data + 448 + 2 * r:data + 452 + 2 * r] = 0
-    return kv_p, kv_c
-
+    return poison_rows(w, 0, slots, seed)
 
 def test_scrub_is_the_identity_on_a_finite_cache():
     w = _w(111)
