@@ -74,6 +74,11 @@ def lib():
             P, ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int64,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P]
         L.orc_convert_req_index_to_global.restype = None
+        L.orc_quantize_row.argtypes = [P, ctypes.c_int32, P, P]
+        L.orc_quantize_row.restype = None
+        L.orc_store_rows.argtypes = [P, ctypes.c_int64, P, ctypes.c_int64, P, ctypes.c_int32,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+        L.orc_store_rows.restype = None
         _lib = L
     return _lib
 
@@ -184,3 +189,27 @@ def convert_req_index_to_global(*, token_indices, block_table, max_blocks_per_re
                                           max_blocks_per_req, _ptr(ti), ti.shape[1], T, width,
                                           block_size, _ptr(cu), invalid_fill, _ptr(out))
     return out[:n_out] if cu is not None else out[:n_out].reshape(T, width)
+
+
+def quantize_row(x_bits: np.ndarray, *, sanitize: bool):
+    """One bf16 row (uint16 bits [512]) -> (576 data bytes, 8 scale bytes)."""
+    x = _c(x_bits, np.uint16)
+    assert x.shape == (512,)
+    data = np.zeros(576, dtype=np.uint8)
+    scales = np.zeros(8, dtype=np.uint8)
+    lib().orc_quantize_row(_ptr(x), 1 if sanitize else 0, _ptr(data), _ptr(scales))
+    return data, scales
+
+
+def store_rows(kv: np.ndarray, rows_bits: np.ndarray, slots: np.ndarray, *, block_size: int,
+               sanitize: bool) -> np.ndarray:
+    """Returns a copy of the pool kv [num_blocks, page_stride] with the bf16
+    rows (uint16 bits [n, 512]) quantised and stored at the global slots."""
+    out = np.array(kv, dtype=np.uint8, copy=True, order="C")
+    rows = _c(rows_bits, np.uint16)
+    sl = _c(slots, np.int64)
+    n = sl.shape[0]
+    assert rows.shape == (n, 512)
+    lib().orc_store_rows(_ptr(rows), 512, _ptr(sl), n, _ptr(out), block_size, out.shape[0],
+                         out.shape[1], 1 if sanitize else 0)
+    return out

@@ -372,3 +372,89 @@ void orc_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
         }
     }
 }
+
+/* ------------------------------------------------------------ cache writer */
+
+/* Nearest E4M3FN code to a finite v with |v| <= 448: the non-negative codes
+ * 0x00..0x7E are the whole finite grid; the closest one wins and a tie goes
+ * to the even code (mantissa LSB 0).  The sign bit is v's, so -0 and
+ * negative values that round to zero give 0x80. */
+static uint8_t orc_encode_e4m3fn(double v) {
+    double a = fabs(v), best_d = INFINITY;
+    int c, best = 0;
+    for (c = 0; c <= 0x7E; ++c) {
+        double d = fabs(orc_e4m3fn((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/* Quantise one 512-wide bf16 row into the fp8_ds_mla row format.
+ *
+ * NoPE group g (dims [64g, 64g+64)): a = the largest |x| of the group, NaN
+ * elements left out; its UE8M0 code is the smallest c in [0, cap] with
+ * a <= 448 * 2^(c-127) (cap when none is), the value divided by the scale
+ * then lands in the FP8 range; each element is stored as the E4M3FN
+ * rounding of x * 2^(127-c) clamped to [-448, 448], a NaN element as 0x7F.
+ * cap = 254 with sanitize, else 255 (a NaN scale).  RoPE dims are stored as
+ * the input bf16; with sanitize a NaN or infinite RoPE value is stored as
+ * +0.  Scale byte 7 is 0.
+ * [vLLM-52212] the sanitising writer snippet (code clamped to [0, 254]
+ * instead of [0, 255]; non-finite RoPE values normalised to 0, so the
+ * decoder can skip its scrub); the smallest-sufficient-code rule is the
+ * reading taken where the pages do not print the amax -> code step. */
+void orc_quantize_row(const uint16_t* x, int32_t sanitize, uint8_t* data, uint8_t* scales) {
+    const int cap = sanitize ? 254 : 255;
+    int g, j, c, r;
+    for (g = 0; g < ORC_DNOPE / 64; ++g) {
+        double a = 0.0;
+        for (j = 64 * g; j < 64 * g + 64; ++j) {
+            double v = orc_bf16(x[j]);
+            if (!isnan(v) && fabs(v) > a) a = fabs(v);
+        }
+        for (c = 0; c < cap; ++c)
+            if (a <= 448.0 * ldexp(1.0, c - 127)) break;
+        scales[g] = (uint8_t)c;
+        for (j = 64 * g; j < 64 * g + 64; ++j) {
+            double v = orc_bf16(x[j]);
+            if (isnan(v)) {
+                data[j] = 0x7F;
+                continue;
+            }
+            v = ldexp(v, 127 - c);
+            if (v > 448.0) v = 448.0;
+            if (v < -448.0) v = -448.0;
+            data[j] = orc_encode_e4m3fn(v);
+        }
+    }
+    scales[7] = 0;
+    for (r = 0; r < ORC_DROPE; ++r) {
+        uint16_t bits = x[ORC_DNOPE + r];
+        if (sanitize && !isfinite(orc_bf16(bits))) bits = 0;
+        data[ORC_DNOPE + 2 * r] = (uint8_t)(bits & 0xFF);
+        data[ORC_DNOPE + 2 * r + 1] = (uint8_t)(bits >> 8);
+    }
+}
+
+/* Store n rows at global slots: slot s is row s % block_size of page
+ * s / block_size (the same addressing the decode reads); a negative slot or
+ * one past the pool is skipped. */
+void orc_store_rows(const uint16_t* rows, int64_t row_stride, const int64_t* slots, int64_t n,
+                    uint8_t* kv, int32_t block_size, int64_t num_blocks, int64_t page_stride,
+                    int32_t sanitize) {
+    int64_t i;
+    for (i = 0; i < n; ++i) {
+        int64_t s = slots[i], page, off;
+        if (s < 0) continue;
+        page = s / block_size;
+        off = s % block_size;
+        if (page >= num_blocks) continue;
+        orc_quantize_row(rows + i * row_stride, sanitize,
+                         kv + page * page_stride + off * ORC_ROW_DATA,
+                         kv + page * page_stride + (int64_t)block_size * ORC_ROW_DATA +
+                             off * ORC_ROW_SCALE);
+    }
+}

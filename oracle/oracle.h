@@ -69,6 +69,17 @@ void orc_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
                                      int32_t block_size, const int32_t* cu_seqlens,
                                      int32_t invalid_fill, int32_t* out);
 
+/* Cache writer: quantise one bf16 row (448 NoPE + 64 RoPE) into 576 data
+ * bytes and 8 scale bytes; sanitize = 1 caps codes at 254 and stores
+ * non-finite RoPE values as 0. */
+void orc_quantize_row(const uint16_t* x, int32_t sanitize, uint8_t* data, uint8_t* scales);
+
+/* Quantise-and-store n rows (bf16, row_stride elements apart) at global
+ * slots; negative slots and slots past the pool are skipped. */
+void orc_store_rows(const uint16_t* rows, int64_t row_stride, const int64_t* slots, int64_t n,
+                    uint8_t* kv, int32_t block_size, int64_t num_blocks, int64_t page_stride,
+                    int32_t sanitize);
+
 #ifdef __cplusplus
 }
 #endif

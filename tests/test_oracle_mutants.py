@@ -18,6 +18,7 @@ import oracle
 from tests import test_oracle_attention as A
 from tests import test_oracle_convert as C
 from tests import test_oracle_decoders as DEC
+from tests import test_oracle_writer as W
 
 MUTANTS = {
     "sink_dropped": ("if (has_sink) D += exp(sink - M);", ""),
@@ -50,6 +51,21 @@ MUTANTS = {
     "scrub_nope_only": ("for (j = 0; j < ORC_D; ++j)\n            if (!isfinite(out[j])) out[j] = 0.0;",
                         "for (j = 0; j < ORC_DNOPE; ++j)\n            if (!isfinite(out[j])) out[j] = 0.0;"),
     "scrub_ignored": ("if (d->scrub)\n", "if (0)\n"),
+    "writer_cap_ignores_sanitize": ("const int cap = sanitize ? 254 : 255;", "const int cap = 255;"),
+    "writer_rope_nan_only": ("if (sanitize && !isfinite(orc_bf16(bits))) bits = 0;",
+                             "if (sanitize && isnan(orc_bf16(bits))) bits = 0;"),
+    "writer_code_strict": ("if (a <= 448.0 * ldexp(1.0, c - 127)) break;",
+                           "if (a < 448.0 * ldexp(1.0, c - 127)) break;"),
+    "writer_code_one_low": ("if (a <= 448.0 * ldexp(1.0, c - 127)) break;",
+                            "if (a <= 448.0 * ldexp(1.0, c - 126)) break;"),
+    "writer_ties_away": ("(d == best_d && (c & 1) == 0 && (best & 1) == 1)", "(d == best_d)"),
+    "writer_nan_sets_scale": ("if (!isnan(v) && fabs(v) > a) a = fabs(v);",
+                              "if (isnan(v) || fabs(v) > a) a = isnan(v) ? INFINITY : fabs(v);"),
+    "writer_sign_of_zero": ("return (uint8_t)(best | (signbit(v) ? 0x80 : 0));",
+                            "return (uint8_t)(best | (v < 0 ? 0x80 : 0));"),
+    "writer_pad_byte": ("scales[7] = 0;", "scales[7] = scales[0];"),
+    "writer_rope_swapped": ("data[ORC_DNOPE + 2 * r] = (uint8_t)(bits & 0xFF);",
+                            "data[ORC_DNOPE + 2 * r] = (uint8_t)(bits >> 8);"),
     "dot_skips_rope": ("for (j = 0; j < ORC_D; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];",
                        "for (j = 0; j < 448; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];"),
 }
@@ -58,7 +74,7 @@ MUTANTS = {
 def _pins():
     """Every test function of the pin modules, expanded over its parameters."""
     out = []
-    for mod in (DEC, A, C):
+    for mod in (DEC, A, C, W):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
@@ -101,7 +117,8 @@ from tests.test_oracle_mutants import _pins
 real = oracle.lib()
 mut = ctypes.CDLL(sys.argv[1])
 for n in ("orc_e4m3fn", "orc_ue8m0", "orc_bf16", "orc_resolve", "orc_dequant_row",
-          "orc_sparse_decode", "orc_convert_req_index_to_global"):
+          "orc_sparse_decode", "orc_convert_req_index_to_global", "orc_quantize_row",
+          "orc_store_rows"):
     f, g = getattr(mut, n), getattr(real, n)
     f.argtypes, f.restype = g.argtypes, g.restype
 oracle._lib = mut
