@@ -244,6 +244,25 @@ def main() -> int:
     tiny = torch.empty(1, dtype=torch.int32, device=dev)
     kt_empty = time_graph(capture(lambda r: tiny.fill_(r), K), K)
 
+    # Cache writer (not part of the decode step): quantise-and-store of a
+    # 65536-row bulk into fresh pages, rotating over replicas of rows and
+    # pages so that each launch reads and writes HBM.
+    wn, wbs = 65536, 64
+    wpages = wn // wbs
+    wrep = max(2, math.ceil(2 * INFINITY_CACHE_BYTES / (wn * (1024 + 584))))
+    wrows = torch.randn((wrep * wn, 512), device=dev).to(torch.bfloat16)
+    wpool = torch.empty((wrep * wpages, wbs * ROW_BYTES), dtype=torch.uint8, device=dev)
+    wslots = torch.stack([torch.randperm(wn, device=dev) + r * wn for r in range(wrep)])
+    wslots = wslots.to(torch.int64)
+
+    def writer(r):
+        dsv4.dsv4_quantize_store(wrows[r * wn:(r + 1) * wn], 512, wslots[r], wn, wpool, wbs,
+                                 wrep * wpages, wbs * ROW_BYTES, dsv4.DSV4_STORE_SANITIZE)
+
+    kt_writer = time_graph(capture(lambda r: writer(r % wrep), K), K)
+    writer_bytes = wn * (512 * 2 + 8 + ROW_BYTES)
+    del wrows, wpool, wslots
+
     # Cache-warm reference: one replica, same step.
     g_hot = capture(lambda r: step(0), K)
     hot_ms_per_step = time_graph(g_hot, K)
@@ -304,6 +323,10 @@ def main() -> int:
         "floors_ms": {"gather_only": kt_gather, "empty_launch": kt_empty,
                       "partial_over_gather": kt_part / kt_gather},
         "event_ms_per_step": ev_ms_per_step,
+        "writer": {"rows": wn, "block_size": wbs, "sanitize": True, "replicas": wrep,
+                   "ms": kt_writer, "algorithmic_bytes": writer_bytes,
+                   "GBps": writer_bytes / (kt_writer * 1e-3) / 1e9,
+                   "frac": writer_bytes / (kt_writer * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "cache_warm": {"ms_per_step": hot_ms_per_step, "decode_partial_ms": kt_part_hot,
                        "tokens_per_s": n_valid / (hot_ms_per_step * 1e-3)},
         "timed_output_matches_single_call": same,

@@ -209,6 +209,44 @@ int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
                         const void* part_out, const float* part_lse, const float* sink,
                         void* out, float* lse, hipStream_t stream);
 
+/* ------------------------------------------------------ cache writer */
+
+/* Store flag: sanitise while quantising (see dsv4_quantize_store). */
+#define DSV4_STORE_SANITIZE 0x1u
+
+/* Quantise bf16 rows and store them into the fp8_ds_mla cache.
+ *
+ * Row i (512 bf16: dims [0, 448) NoPE, [448, 512) RoPE) goes to global slot
+ * s = slot_mapping[i]: row s % block_size of page s / block_size, in the
+ * page layout above.  For NoPE group g (dims [64g, 64g+64)) let a be the
+ * largest |x| of the group, NaN elements left out; its UE8M0 code is the
+ * smallest c in [0, cap] with a <= 448 * 2^(c-127) (cap when none is, i.e.
+ * for an infinity), and each element is stored as the E4M3FN rounding
+ * (nearest, ties to even) of x * 2^(127-c) clamped to [-448, 448]; a NaN
+ * element stores 0x7F.  RoPE values are stored bit for bit.  Scale byte 7
+ * is 0.  With DSV4_STORE_SANITIZE, cap = 254 and a NaN or infinite RoPE
+ * value is stored as +0, so that a cache written from finite NoPE inputs
+ * holds no non-finite value and decodes without DSV4_DECODE_SCRUB;
+ * without it cap = 255 (a NaN scale).  (vLLM PR #52212 page, the sanitising
+ * writer snippet: code clamp [0, 254] vs [0, 255], RoPE non-finite -> 0.
+ * The amax -> code rule is not printed there; the smallest sufficient code
+ * is the reading taken.)
+ *
+ * Arguments (device pointers, caller-owned):
+ *   rows          bf16 [num_rows, row_stride], 16-byte aligned,
+ *                 row_stride a multiple of 8 and >= 512
+ *   slot_mapping  int64 [num_rows]; a negative slot or one past the pool
+ *                 (s / block_size >= num_blocks) skips its row
+ *   kv_cache      uint8 [num_blocks, page_stride], 8-byte aligned,
+ *                 page_stride a multiple of 8 and >= block_size * 584
+ *   flags         0 or DSV4_STORE_SANITIZE
+ * Only the 576 data bytes and 8 scale bytes of each stored row are
+ * written.  Slots must be distinct: rows sharing a slot race, and the bytes
+ * left there are unspecified.  num_rows = 0 launches nothing. */
+int dsv4_quantize_store(const void* rows, int64_t row_stride, const int64_t* slot_mapping,
+                        int64_t num_rows, void* kv_cache, int32_t block_size, int64_t num_blocks,
+                        int64_t page_stride, uint32_t flags, hipStream_t stream);
+
 /* ------------------------------------------------- index conversion */
 
 /* Req-local -> global slot conversion through a block table.  For token t

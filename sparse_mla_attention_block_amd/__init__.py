@@ -32,6 +32,7 @@ DSV4_ERR_WORKSPACE_TOO_SMALL = 3
 DSV4_ERR_HIP = 4
 MAX_SPLITS = 64
 DSV4_DECODE_SCRUB = 0x1
+DSV4_STORE_SANITIZE = 0x1
 
 
 class dsv4_decode_desc(ctypes.Structure):
@@ -94,6 +95,9 @@ _lib.dsv4_convert_req_index_to_global.argtypes = [
 _lib.dsv4_convert_req_index_to_global.restype = ctypes.c_int
 _lib.dsv4_gather_floor.argtypes = [_DESC, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
 _lib.dsv4_gather_floor.restype = ctypes.c_int
+_lib.dsv4_quantize_store.argtypes = [_P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int32,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, _P]
+_lib.dsv4_quantize_store.restype = ctypes.c_int
 
 
 class Dsv4Error(RuntimeError):
@@ -194,6 +198,14 @@ def dsv4_convert_req_index_to_global(req_id: Optional[torch.Tensor], num_reqs: i
         _ptr(req_id), num_reqs, _ptr(block_table), bt_stride, max_blocks_per_req,
         _ptr(token_indices), ti_stride, num_tokens, width, block_size, _ptr(cu_seqlens),
         invalid_fill, _ptr(out), _stream(stream)))
+
+
+def dsv4_quantize_store(rows: torch.Tensor, row_stride: int, slot_mapping: torch.Tensor,
+                        num_rows: int, kv_cache: torch.Tensor, block_size: int, num_blocks: int,
+                        page_stride: int, flags: int = DSV4_STORE_SANITIZE, stream=None) -> None:
+    _check(_lib.dsv4_quantize_store(_ptr(rows), row_stride, _ptr(slot_mapping), num_rows,
+                                    _ptr(kv_cache), block_size, num_blocks, page_stride, flags,
+                                    _stream(stream)))
 
 
 def dsv4_gather_floor(desc, kv_cache: torch.Tensor, block_table: Optional[torch.Tensor],

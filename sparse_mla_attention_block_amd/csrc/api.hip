@@ -358,4 +358,43 @@ int dsv4_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
     return launched(dsv4::launch_convert(p, stream), "convert");
 }
 
+int dsv4_quantize_store(const void* rows, int64_t row_stride, const int64_t* slot_mapping,
+                        int64_t num_rows, void* kv_cache, int32_t block_size, int64_t num_blocks,
+                        int64_t page_stride, uint32_t flags, hipStream_t stream) {
+    if (num_rows < 0) return fail(DSV4_ERR_INVALID_ARGUMENT, "num_rows must be >= 0");
+    if (flags & ~DSV4_STORE_SANITIZE)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "unknown store flags 0x%x",
+                    (unsigned)(flags & ~DSV4_STORE_SANITIZE));
+    if (block_size < 1) return fail(DSV4_ERR_INVALID_ARGUMENT, "block_size must be >= 1");
+    if (num_blocks < 1) return fail(DSV4_ERR_INVALID_ARGUMENT, "num_blocks must be >= 1");
+    if (page_stride < (int64_t)block_size * dsv4::kRowBytes || page_stride % 8)
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "page_stride must be a multiple of 8 and >= block_size*584 = %lld (got %lld)",
+                    (long long)block_size * dsv4::kRowBytes, (long long)page_stride);
+    if (num_blocks > INT64_MAX / page_stride)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "num_blocks * page_stride overflows");
+    if (row_stride < dsv4::kD || row_stride % 8)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "row_stride must be a multiple of 8 and >= 512");
+    if (num_rows == 0) return ok();
+    if (!rows || !slot_mapping || !kv_cache)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "rows, slot_mapping and kv_cache must not be NULL");
+    if (!aligned(rows, 16)) return fail(DSV4_ERR_INVALID_ARGUMENT, "rows must be 16-byte aligned");
+    if (!aligned(slot_mapping, 8))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte aligned");
+    if (!aligned(kv_cache, 8)) return fail(DSV4_ERR_INVALID_ARGUMENT, "kv_cache must be 8-byte aligned");
+    if ((num_rows + 3) / 4 > INT32_MAX) return fail(DSV4_ERR_INVALID_ARGUMENT, "num_rows too large");
+    dsv4::StoreParams p;
+    p.rows = static_cast<const uint16_t*>(rows);
+    p.slots = slot_mapping;
+    p.kv = static_cast<uint8_t*>(kv_cache);
+    p.n = num_rows;
+    p.row_stride = row_stride;
+    p.num_blocks = num_blocks;
+    p.page_stride = page_stride;
+    p.bs = block_size;
+    p.sanitize = (flags & DSV4_STORE_SANITIZE) ? 1 : 0;
+    (void)hipGetLastError();
+    return launched(dsv4::launch_quantize_store(p, stream), "quantize store");
+}
+
 }  // extern "C"

@@ -176,18 +176,6 @@ __device__ __forceinline__ void load_patch(PatchSrc a, int l8, uint32_t (&rr)[64
     rr[O + 19] = (uint32_t)(sw >> 32);
 }
 
-// Two bf16 with any NaN or infinite half replaced by +0.  A half is not
-// finite when its magnitude bits are >= 0x7F80 (all exponent bits set);
-// adding 0x80 to the magnitude then sets bit 15 of that half, with no carry
-// into the other half, and an arithmetic shift by 15 spreads bit 15 into a
-// half-wide mask.
-__device__ __forceinline__ uint32_t scrub_pair(uint32_t w) {
-    typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
-    const uint32_t t = (w & 0x7FFF7FFFu) + 0x00800080u;
-    const uint32_t bad = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, t) >> (int16_t)15);
-    return w & ~bad;
-}
-
 // Dequantises the chunks into the K tile.  With SCRUB every element that is
 // not finite after dequantisation (an FP8 NaN byte, a NaN scale code, a
 // product past the bf16 range, a NaN or infinite RoPE value) is stored as 0.

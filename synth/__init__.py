@@ -17,6 +17,7 @@ from .workloads import (  # noqa: F401
     Workload,
     make_workload,
     make_custom,
+    make_writer_rows,
     poison_rows,
     workload_digest,
 )

@@ -305,3 +305,49 @@ def poison_rows(w: Workload, b: int, slots: Sequence[int], seed: int, base=None)
         kv_p[pg, data + r:data + r + 4] = [0xC0, 0x7F, 0x80, 0xFF]   # bf16 NaN, bf16 -inf
         kv_c[pg, data + r:data + r + 4] = 0
     return kv_p, kv_c
+
+
+def make_writer_rows(n: int, seed: int, *, specials: bool = True, spread: int = 30) -> np.ndarray:
+    """Seeded bf16 rows (uint16 bits [n, 512]) for the cache writer: each
+    64-dim NoPE group is N(0,1) times its own power of two drawn from
+    [2^-spread, 2^spread] (at 30 the UE8M0 codes spread over ~60 values),
+    RoPE is N(0,1).  With ``specials``, one row in 8 also gets a special group:
+    all zeros, a lone +-inf, NaN elements, bf16 subnormals, the bf16 maximum,
+    exact E4M3FN ties, +-0 mixtures or values near 2^100, and one row in 16
+    a NaN or infinite RoPE value."""
+    rng = np.random.default_rng(seed)
+    x = np.empty((n, 512), dtype=np.float32)
+    scale = 2.0 ** rng.integers(-spread, spread + 1, size=(n, 7)).astype(np.float32)
+    x[:, :448] = (rng.standard_normal((n, 7, 64)).astype(np.float32) * scale[:, :, None]).reshape(n, 448)
+    x[:, 448:] = rng.standard_normal((n, 64)).astype(np.float32)
+    bits = _bf16_bits(x)
+    if specials:
+        for i in range(0, n, 8):
+            g = int(rng.integers(0, 7))
+            grp = slice(64 * g, 64 * g + 64)
+            kind = int(rng.integers(0, 8))
+            if kind == 0:
+                bits[i, grp] = 0
+            elif kind == 1:
+                bits[i, 64 * g + int(rng.integers(0, 64))] = 0x7F80 if rng.random() < 0.5 else 0xFF80
+            elif kind == 2:
+                bits[i, 64 * g + rng.choice(64, 3, replace=False)] = [0x7FC0, 0xFFC1, 0x7F81]
+            elif kind == 3:
+                bits[i, grp] = rng.integers(0, 0x80, size=64).astype(np.uint16) | \
+                    (rng.integers(0, 2, size=64).astype(np.uint16) << 15)
+            elif kind == 4:
+                bits[i, 64 * g] = 0x7F7F
+            elif kind == 5:
+                # 448 fixes the scale at 1; the rest are midpoints of E4M3FN steps
+                bits[i, 64 * g] = 0x43E0
+                m = rng.integers(0, 8, size=63)
+                e = rng.integers(-6, 8, size=63)
+                v = (1.0 + (2 * m + 1) / 16.0) * 2.0 ** e
+                bits[i, 64 * g + 1:64 * g + 64] = _bf16_bits(v.astype(np.float32))
+            elif kind == 6:
+                bits[i, grp] = np.where(rng.random(64) < 0.5, 0x0000, 0x8000)
+            else:
+                bits[i, grp] = _bf16_bits((rng.standard_normal(64) * 2.0 ** 100).astype(np.float32))
+            if i % 16 == 0:
+                bits[i, 448 + int(rng.integers(0, 64))] = [0x7FC0, 0x7F80, 0xFF80][int(rng.integers(0, 3))]
+    return bits

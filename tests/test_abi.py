@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     for want in ("dsv4_sparse_decode", "dsv4_sparse_decode_partial", "dsv4_combine_splits",
                  "dsv4_convert_req_index_to_global", "dsv4_sparse_decode_plan",
                  "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error",
-                 "dsv4_gather_floor"):
+                 "dsv4_gather_floor", "dsv4_quantize_store"):
         assert want in names
 
 
@@ -202,3 +202,22 @@ def test_decode_rejects_null_and_missing_workspace_without_touching_the_gpu():
     assert dsv4._lib.dsv4_combine_splits(1, 64, 0, fake, fake, None, fake, None, None) == \
         dsv4.DSV4_ERR_INVALID_ARGUMENT
     assert dsv4.dsv4_status_string(3) == "DSV4_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_writer_validation_without_touching_the_gpu():
+    lib = dsv4._lib
+    fake = ctypes.c_void_p(4096)
+    E = dsv4.DSV4_ERR_INVALID_ARGUMENT
+    S = dsv4.DSV4_STORE_SANITIZE
+    assert lib.dsv4_quantize_store(fake, 512, fake, 0, fake, 64, 10, 64 * 584, S, None) == 0
+    assert lib.dsv4_quantize_store(None, 512, fake, 4, fake, 64, 10, 64 * 584, S, None) == E
+    assert lib.dsv4_quantize_store(fake, 512, fake, 4, fake, 64, 10, 64 * 584, 0x2, None) == E
+    assert "flags" in dsv4.dsv4_last_error()
+    assert lib.dsv4_quantize_store(fake, 500, fake, 4, fake, 64, 10, 64 * 584, S, None) == E
+    assert lib.dsv4_quantize_store(fake, 516, fake, 4, fake, 64, 10, 64 * 584, S, None) == E
+    assert lib.dsv4_quantize_store(fake, 512, fake, 4, fake, 64, 10, 64 * 584 - 8, S, None) == E
+    assert lib.dsv4_quantize_store(fake, 512, fake, 4, fake, 0, 10, 64 * 584, S, None) == E
+    assert lib.dsv4_quantize_store(fake, 512, fake, 4, fake, 64, 0, 64 * 584, S, None) == E
+    assert lib.dsv4_quantize_store(ctypes.c_void_p(4104), 512, fake, 4, fake, 64, 10, 64 * 584,
+                                   S, None) == E          # rows misaligned
+    assert lib.dsv4_quantize_store(fake, 512, fake, -1, fake, 64, 10, 64 * 584, S, None) == E
