@@ -245,15 +245,18 @@ def main() -> int:
     kt_empty = time_graph(capture(lambda r: tiny.fill_(r), K), K)
 
     # Cache writer (not part of the decode step): quantise-and-store of a
-    # 65536-row bulk into fresh pages, rotating over replicas of rows and
-    # pages so that each launch reads and writes HBM.
+    # 65536-row bulk, rotating over replicas of rows and pages so that each
+    # launch reads and writes HBM.
     wn, wbs = 65536, 64
     wpages = wn // wbs
     wrep = max(2, math.ceil(2 * INFINITY_CACHE_BYTES / (wn * (1024 + 584))))
     wrows = torch.randn((wrep * wn, 512), device=dev).to(torch.bfloat16)
     wpool = torch.empty((wrep * wpages, wbs * ROW_BYTES), dtype=torch.uint8, device=dev)
-    wslots = torch.stack([torch.randperm(wn, device=dev) + r * wn for r in range(wrep)])
-    wslots = wslots.to(torch.int64)
+    # A prefill-like chunk: consecutive rows fill whole pages in order, the
+    # pages themselves drawn in shuffled order from the pool.
+    pos = torch.arange(wn, device=dev)
+    wslots = torch.stack([torch.randperm(wpages, device=dev)[pos // wbs] * wbs + pos % wbs
+                          + r * wn for r in range(wrep)]).to(torch.int64)
 
     def writer(r):
         dsv4.dsv4_quantize_store(wrows[r * wn:(r + 1) * wn], 512, wslots[r], wn, wpool, wbs,

@@ -390,6 +390,7 @@ int dsv4_quantize_store(const void* rows, int64_t row_stride, const int64_t* slo
     p.n = num_rows;
     p.row_stride = row_stride;
     p.num_blocks = num_blocks;
+    p.num_slots = num_blocks * block_size;
     p.page_stride = page_stride;
     p.bs = block_size;
     p.sanitize = (flags & DSV4_STORE_SANITIZE) ? 1 : 0;

@@ -107,6 +107,7 @@ struct StoreParams {
     int64_t n;
     int64_t row_stride;         // elements
     int64_t num_blocks;
+    int64_t num_slots;          // num_blocks * bs
     int64_t page_stride;
     int32_t bs;
     int32_t sanitize;

@@ -5,7 +5,8 @@
 // the pages; the code taken is the smallest one whose scale brings the
 // group's largest magnitude within the E4M3FN range (|v| <= 448).
 //
-// One wave per row, 4 rows per workgroup.  Lane l holds dims [8l, 8l+8):
+// Each wave quantises 2 consecutive rows (8 per workgroup), one at a time
+// after loading both.  Lane l holds dims [8l, 8l+8) of a row:
 // lanes 0..55 the seven 64-dim NoPE groups (8 lanes each), lanes 56..63 the
 // RoPE dims.  The group maximum is taken on bf16 magnitude bits (integer
 // order equals magnitude order; NaN is dropped first), so the code is exact
@@ -18,7 +19,8 @@
 namespace dsv4 {
 
 constexpr int kStoreThreads = 256;
-constexpr int kStoreRows = kStoreThreads / 64;
+constexpr int kStoreRowsPerWave = 2;
+constexpr int kStoreRows = kStoreThreads / 64 * kStoreRowsPerWave;   // per workgroup
 
 // Smallest UE8M0 code c with a <= 448 * 2^(c-127) for the bf16 magnitude
 // bits a (NaN excluded), clamped to [0, cap].  With a = (1 + M/128) 2^(E-127)
@@ -48,24 +50,13 @@ __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, int c) {
     return out;
 }
 
-__global__ __launch_bounds__(kStoreThreads) void quantize_store_kernel(const StoreParams p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kStoreRows + (threadIdx.x >> 6);
-    if (row >= p.n) return;                       // whole waves leave together
-    const int64_t slot = p.slots[row];
-    if (slot < 0) return;
-    const int64_t page = slot / p.bs;
-    if (page >= p.num_blocks) return;
-    const int64_t off = slot - page * p.bs;
-    uint8_t* base = p.kv + page * p.page_stride;
-    uint8_t* data = base + off * kRowData;
-    uint8_t* scale = base + (int64_t)p.bs * kRowData + off * kRowScale;
-
-    const uint4 in = *reinterpret_cast<const uint4*>(p.rows + row * p.row_stride + 8 * lane);
+// Quantises the row whose 8 bf16 values this lane holds and stores it at
+// `slot` (a skipped slot stores nothing; the caller's branch is wave-uniform).
+__device__ __forceinline__ void store_row(const StoreParams& p, int lane, int64_t slot,
+                                          const uint4 in) {
     const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-
-    // Largest finite-or-infinite magnitude of the lane's 8 values, then of its
-    // 8-lane group (xor 1, 2, 4 stay inside aligned groups of 8).
+    // Largest finite-or-infinite magnitude of the lane's 8 values, then of
+    // its 8-lane group (xor 1, 2, 4 stay inside aligned groups of 8).
     uint32_t a = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -76,9 +67,21 @@ __global__ __launch_bounds__(kStoreThreads) void quantize_store_kernel(const Sto
     a = max(a, (uint32_t)__shfl_xor((int)a, 1));
     a = max(a, (uint32_t)__shfl_xor((int)a, 2));
     a = max(a, (uint32_t)__shfl_xor((int)a, 4));
-    const int cap = p.sanitize ? 254 : 255;
-    const int c = ue8m0_code(a, cap);
+    const int c = ue8m0_code(a, p.sanitize ? 254 : 255);
 
+    // Page and offset: 32-bit division when every slot fits in 32 bits (a
+    // wave-uniform branch on the pool size), 64-bit otherwise.
+    int64_t page, off;
+    if (p.num_slots <= 0xFFFFFFFFll) {
+        const uint32_t s32 = (uint32_t)slot, q = s32 / (uint32_t)p.bs;
+        page = q;
+        off = s32 - q * (uint32_t)p.bs;
+    } else {
+        page = slot / p.bs;
+        off = slot - page * p.bs;
+    }
+    uint8_t* base = p.kv + page * p.page_stride;
+    uint8_t* data = base + off * kRowData;
     if (lane < kDNope / 8) {
         *reinterpret_cast<uint2*>(data + 8 * lane) =
             make_uint2(quant4(w[0], w[1], c), quant4(w[2], w[3], c));
@@ -97,7 +100,34 @@ __global__ __launch_bounds__(kStoreThreads) void quantize_store_kernel(const Sto
 #pragma unroll
     for (int g = 0; g < kDNope / 64; ++g)
         sw |= (uint64_t)(uint32_t)__builtin_amdgcn_readlane(c, 8 * g) << (8 * g);
-    if (lane == 0) *reinterpret_cast<uint2*>(scale) = make_uint2((uint32_t)sw, (uint32_t)(sw >> 32));
+    if (lane == 0)
+        *reinterpret_cast<uint2*>(base + (int64_t)p.bs * kRowData + off * kRowScale) =
+            make_uint2((uint32_t)sw, (uint32_t)(sw >> 32));
+}
+
+// Each wave takes kStoreRowsPerWave consecutive rows and issues all their
+// loads before the first store, so that every wave keeps that many 1 KB
+// rows in flight.
+__global__ __launch_bounds__(kStoreThreads) void quantize_store_kernel(const StoreParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row0 =
+        ((int64_t)blockIdx.x * (kStoreThreads / 64) + (threadIdx.x >> 6)) * kStoreRowsPerWave;
+    if (row0 >= p.n) return;                      // whole waves leave together
+    uint4 in[kStoreRowsPerWave];
+    int64_t slot[kStoreRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kStoreRowsPerWave; ++i) {
+        const int64_t r = row0 + i < p.n ? row0 + i : p.n - 1;   // tail rows re-read the last
+        // The slot is the same for the whole wave: keep it in scalar registers.
+        const int64_t s_ld = p.slots[r];
+        const int64_t s = row0 + i < p.n ? s_ld : -1;
+        slot[i] = (int64_t)((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(s >> 32)) << 32 |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)s));
+        in[i] = *reinterpret_cast<const uint4*>(p.rows + r * p.row_stride + 8 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < kStoreRowsPerWave; ++i)
+        if (slot[i] >= 0 && slot[i] < p.num_slots) store_row(p, lane, slot[i], in[i]);
 }
 
 hipError_t launch_quantize_store(const StoreParams& p, hipStream_t stream) {
