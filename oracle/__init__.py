@@ -46,6 +46,7 @@ class OrcDesc(ctypes.Structure):
         ("page_stride", ctypes.c_int64),
         ("sm_scale", ctypes.c_double),
         ("scrub", ctypes.c_int32),
+        ("s_q", ctypes.c_int32),
     ]
 
 
@@ -109,14 +110,14 @@ def bf16(bits: int) -> float:
 
 
 def make_desc(*, B, H, topk, swa, block_size, num_blocks, page_stride, sm_scale,
-              block_table=None, max_blocks_per_seq=None, scrub=False) -> OrcDesc:
+              block_table=None, max_blocks_per_seq=None, scrub=False, s_q=1) -> OrcDesc:
     if block_table is not None:
         bt_stride = block_table.shape[1]
         mb = bt_stride if max_blocks_per_seq is None else max_blocks_per_seq
     else:
         bt_stride, mb = 0, 0
     return OrcDesc(B, H, topk, swa, block_size, mb, num_blocks, bt_stride, page_stride,
-                   float(sm_scale), 1 if scrub else 0)
+                   float(sm_scale), 1 if scrub else 0, int(s_q))
 
 
 def resolve(desc: OrcDesc, block_table, b: int, idx: int):
@@ -137,9 +138,10 @@ def dequant_row(desc: OrcDesc, kv: np.ndarray, page: int, off: int) -> np.ndarra
 
 def sparse_decode(*, q, kv, topk_idx, topk, swa, block_size, num_blocks, page_stride,
                   sm_scale, block_table=None, max_blocks_per_seq=None, valid_len=None,
-                  sink=None, num_splits=0, nthreads=None, scrub=False):
+                  sink=None, num_splits=0, nthreads=None, scrub=False, s_q=1):
     """Returns (out [B,H,512] f64, lse [B,H] f64, number of valid entries).
-    scrub: read every non-finite dequantised cache element as 0."""
+    scrub: read every non-finite dequantised cache element as 0.  s_q: query
+    tokens per sequence (block_table and valid_len have B / s_q rows)."""
     q = _c(q, np.uint16)
     B, H, D = q.shape
     assert D == 512
@@ -151,7 +153,8 @@ def sparse_decode(*, q, kv, topk_idx, topk, swa, block_size, num_blocks, page_st
     sk = _c(sink, np.float32)
     desc = make_desc(B=B, H=H, topk=topk, swa=swa, block_size=block_size,
                      num_blocks=num_blocks, page_stride=page_stride, sm_scale=sm_scale,
-                     block_table=bt, max_blocks_per_seq=max_blocks_per_seq, scrub=scrub)
+                     block_table=bt, max_blocks_per_seq=max_blocks_per_seq, scrub=scrub,
+                     s_q=s_q)
     out = np.zeros((B, H, 512), dtype=np.float64)
     lse = np.zeros((B, H), dtype=np.float64)
     n = lib().orc_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(bt), _ptr(ti),
@@ -168,7 +171,7 @@ def decode_workload(w, *, topk_idx=None, use_block_table=True, num_splits=0, nth
               page_stride=w.page_stride, sm_scale=w.sm_scale,
               block_table=w.block_table if use_block_table else None,
               max_blocks_per_seq=w.max_blocks_per_seq if use_block_table else None,
-              valid_len=w.valid_len, sink=w.sink)
+              valid_len=w.valid_len, sink=w.sink, s_q=getattr(w, "s_q", 1))
     kw.update(overrides)
     return sparse_decode(num_splits=num_splits, nthreads=nthreads, **kw)
 

@@ -279,7 +279,11 @@ static void* orc_worker(void* arg) {
     for (it = J->item_begin; it < J->item_end; ++it) {
         int32_t b = (int32_t)(it / d->H), h = (int32_t)(it % d->H);
         if (b != cur_b) {
-            int32_t vl = eff_main_len(d, J->valid_len, b), p;
+            /* The s_q query tokens of a sequence share its block-table row
+             * and top-k length ([SGL-26208] gather+dequant kernel: the
+             * length of token t is read at t // s_q). */
+            const int32_t seq = d->s_q > 1 ? b / d->s_q : b;
+            int32_t vl = eff_main_len(d, J->valid_len, seq), p;
             cur_b = b;
             eff_len = vl + d->swa;
             for (p = 0; p < eff_len; ++p) {
@@ -287,7 +291,7 @@ static void* orc_worker(void* arg) {
                 int32_t idx = J->idx[(int64_t)b * Kt + col];
                 int64_t page;
                 int32_t off;
-                valid[p] = (unsigned char)orc_resolve(d, J->bt, b, idx, &page, &off);
+                valid[p] = (unsigned char)orc_resolve(d, J->bt, seq, idx, &page, &off);
                 if (valid[p]) orc_dequant_row(d, J->kv, page, off, rows + (int64_t)p * ORC_D);
             }
             if (h == 0)

@@ -33,6 +33,9 @@ typedef struct {
     double sm_scale;             /* softmax scale on q.k (not on the sink)   */
     int32_t scrub;               /* 1: every dequantised element that is not
                                     finite is read as 0 (decode-time scrub)  */
+    int32_t s_q;                 /* query tokens per sequence (<= 1: one);
+                                    token b reads block-table row and
+                                    valid_len entry b / s_q                  */
 } orc_desc;
 
 /* Scalar decoders. */

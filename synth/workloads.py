@@ -71,18 +71,19 @@ class Workload:
     num_blocks: int
     max_blocks_per_seq: int
     page_stride: int
-    seq_lens: np.ndarray          # int64 [B]
+    seq_lens: np.ndarray          # int64 [B / s_q]
     q: np.ndarray                 # uint16 [B, H, 512], bf16 bit patterns
     kv: np.ndarray                # uint8 [num_blocks, page_stride]
-    block_table: np.ndarray       # int32 [B, max_blocks_per_seq], -1 = unused
+    block_table: np.ndarray       # int32 [B / s_q, max_blocks_per_seq], -1 = unused
     topk_idx: np.ndarray          # int32 [B, topk + swa], req-local slots, -1 = invalid
-    valid_len: Optional[np.ndarray]  # int32 [B] or None
+    valid_len: Optional[np.ndarray]  # int32 [B / s_q] or None
     sink: Optional[np.ndarray]    # float32 [H] or None
     sm_scale: float               # an exact fp32 value
     num_splits: int               # 0 = let the library choose
     # With keep_floats: (seq, slot, codes [n,7], NoPE values before FP8
     # rounding [n,448] as float32, RoPE values before bf16 rounding [n,64]).
     source_rows: Optional[tuple] = None
+    s_q: int = 1                  # query tokens per sequence: B = sequences * s_q
 
     @property
     def Kt(self) -> int:
@@ -109,15 +110,18 @@ def make_custom(*, B: int, H: int, topk: int, swa: int, seq_lens: Sequence[int],
                 valid_len_range: Optional[tuple] = None, with_sink: bool = True,
                 page_pad: int = 0, slack_frac: float = 0.02, num_splits: int = 0,
                 poison_masked_rows: bool = False, name: str = "custom",
-                keep_floats: bool = False,
+                keep_floats: bool = False, s_q: int = 1,
                 rng: Optional[np.random.Generator] = None) -> Workload:
-    """Build one seeded workload.
+    """Build one seeded workload of B sequences and B * s_q query tokens.
 
-    ``seq_lens`` gives the slot count of every sequence.  Main indices are
-    drawn uniformly without replacement from each sequence's slots (all of
-    them when the sequence is shorter than ``topk``, the rest -1); exactly
+    ``seq_lens`` gives the slot count of every sequence.  Query token j of a
+    sequence of length L (multi-token decode: the sequence's last s_q
+    positions) sits at position P = L - s_q + j and sees slots [0, P].  Its
+    main indices are drawn uniformly without replacement from those slots
+    (all of them when fewer than ``topk``, the rest -1); exactly
     round(invalid_frac*topk) main positions are then set to -1; the SWA part
-    is the last ``swa`` slots, ascending.  With ``poison_masked_rows`` the
+    is the last ``swa`` visible slots, ascending.  With s_q = 1 this is the
+    whole sequence.  With ``poison_masked_rows`` the
     rows that only masked-tail entries (past ``valid_len``) name keep their
     0xFF poison instead of data.
     """
@@ -140,38 +144,39 @@ def make_custom(*, B: int, H: int, topk: int, swa: int, seq_lens: Sequence[int],
         block_table[b, :n] = perm[cursor:cursor + n]
         cursor += n
 
-    # Index lists: [main top-k | SWA], req-local slots.
-    topk_idx = np.full((B, Kt), -1, dtype=np.int32)
+    # Index lists: [main top-k | SWA], req-local slots, one per query token.
+    T = B * s_q
+    topk_idx = np.full((T, Kt), -1, dtype=np.int32)
     n_invalid = _round_half_up(invalid_frac * topk)
-    for b in range(B):
-        L = int(seq_lens[b])
-        n = min(topk, L)
-        topk_idx[b, :n] = rng.choice(L, size=n, replace=False)
+    for t in range(T):
+        L = int(seq_lens[t // s_q]) - s_q + t % s_q + 1      # visible slots
+        n = min(topk, max(L, 0))
+        topk_idx[t, :n] = rng.choice(L, size=n, replace=False) if n else []
         if n_invalid:
             pos = rng.choice(topk, size=n_invalid, replace=False)
-            topk_idx[b, pos] = -1
+            topk_idx[t, pos] = -1
         for j in range(swa):
             p = L - swa + j
-            topk_idx[b, topk + j] = p if p >= 0 else -1
+            topk_idx[t, topk + j] = p if p >= 0 else -1
 
     valid_len = None
     if valid_len_range is not None:
         lo, hi = valid_len_range
         valid_len = rng.integers(lo, hi + 1, size=B).astype(np.int32)
 
-    q = _bf16_bits(rng.standard_normal((B, H, D_QK), dtype=np.float32))
+    q = _bf16_bits(rng.standard_normal((T, H, D_QK), dtype=np.float32))
     sink = rng.standard_normal(H).astype(np.float32) if with_sink else None
     sm_scale = float(np.float32(D_QK ** -0.5))
 
     # Rows for every referenced (sequence, slot) pair, in a fixed order.
     ref_b, ref_slot = [], []
     for b in range(B):
-        row = topk_idx[b]
-        keep = row >= 0
+        rows_b = topk_idx[b * s_q:(b + 1) * s_q]
+        keep = rows_b >= 0
         if poison_masked_rows and valid_len is not None:
             vl = int(np.clip(valid_len[b], 0, topk))
-            keep = keep & ((np.arange(Kt) < vl) | (np.arange(Kt) >= topk))
-        u = np.unique(row[keep].astype(np.int64))
+            keep = keep & ((np.arange(Kt) < vl) | (np.arange(Kt) >= topk))[None, :]
+        u = np.unique(rows_b[keep].astype(np.int64))
         ref_b.append(np.full(u.shape, b, dtype=np.int64))
         ref_slot.append(u)
     ref_b = np.concatenate(ref_b) if ref_b else np.zeros(0, np.int64)
@@ -199,12 +204,12 @@ def make_custom(*, B: int, H: int, topk: int, swa: int, seq_lens: Sequence[int],
         flat[d0[:, None] + np.arange(ROW_DATA_BYTES)[None, :]] = data
         flat[s0[:, None] + np.arange(ROW_SCALE_BYTES)[None, :]] = sc
 
-    return Workload(name=name, seed=seed, B=B, H=H, topk=topk, swa=swa, block_size=bs,
+    return Workload(name=name, seed=seed, B=T, H=H, topk=topk, swa=swa, block_size=bs,
                     num_blocks=pool, max_blocks_per_seq=max_blocks, page_stride=page_stride,
                     seq_lens=seq_lens, q=q, kv=kv, block_table=block_table, topk_idx=topk_idx,
                     valid_len=valid_len, sink=sink, sm_scale=sm_scale, num_splits=num_splits,
                     source_rows=((ref_b, ref_slot, codes, nope_x.astype(np.float32), rope_n)
-                                 if keep_floats else None))
+                                 if keep_floats else None), s_q=s_q)
 
 
 def make_workload(config: int, *, seed: Optional[int] = None, block_size: int = 64,

@@ -36,9 +36,11 @@ def _source_row_table(w):
 
 
 def _entry_mask(w, b):
+    """Taking-part columns of token b (its sequence's top-k length applies)."""
     Kt = w.topk + w.swa
     cols = np.arange(Kt)
-    vl = w.topk if w.valid_len is None else int(np.clip(w.valid_len[b], 0, w.topk))
+    r = b // w.s_q
+    vl = w.topk if w.valid_len is None else int(np.clip(w.valid_len[r], 0, w.topk))
     return (w.topk_idx[b] >= 0) & ((cols < vl) | (cols >= w.topk))
 
 
@@ -53,7 +55,7 @@ def sdpa_reference(w, sink_bias_when_none=0.0):
         K = np.zeros((Kt + 1, 512))
         for k in range(Kt):
             if m[k]:
-                K[k] = table[(b, int(w.topk_idx[b, k]))]
+                K[k] = table[(b // w.s_q, int(w.topk_idx[b, k]))]
         bias = np.full((H, Kt + 1), -np.inf)
         bias[:, :Kt][:, m] = 0.0
         c = w.sink.astype(np.float64) if w.sink is not None else np.full(H, sink_bias_when_none)
@@ -288,3 +290,26 @@ def test_scrub_reads_non_finite_elements_as_zero(S):
     assert np.all(np.isfinite(o_s)) and np.array_equal(o_s, o_c) and np.array_equal(l_s, l_c)
     o_u, _, _ = oracle.decode_workload(w, kv=kv_p, num_splits=S)
     assert np.isnan(o_u[0]).any() and np.array_equal(o_u[1], o_c[1])
+
+
+@pytest.mark.parametrize("s_q", [2, 3])
+def test_multi_token_decode_matches_sdpa(s_q):
+    """s_q query tokens per sequence, each with its own causal top-k list,
+    sharing the sequence's block table and top-k length."""
+    w = _w(120 + s_q, s_q=s_q)
+    assert w.B == 3 * s_q and w.block_table.shape[0] == 3
+    out, lse, _ = oracle.decode_workload(w)
+    ro, rl = sdpa_reference(w)
+    np.testing.assert_allclose(out, ro, rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(lse, rl, rtol=RTOL, atol=ATOL)
+
+
+def test_multi_token_equals_single_token_with_expanded_tables():
+    """Repeating each sequence's block-table row and top-k length once per
+    token and calling with s_q = 1 gives the identical result."""
+    w = _w(125, s_q=4, block_size=16)
+    out, lse, n = oracle.decode_workload(w)
+    bt = np.repeat(w.block_table, 4, axis=0)
+    vl = np.repeat(w.valid_len, 4)
+    o1, l1, n1 = oracle.decode_workload(w, block_table=bt, valid_len=vl, s_q=1)
+    assert n == n1 and np.array_equal(out, o1) and np.array_equal(lse, l1)

@@ -66,6 +66,10 @@ MUTANTS = {
     "writer_pad_byte": ("scales[7] = 0;", "scales[7] = scales[0];"),
     "writer_rope_swapped": ("data[ORC_DNOPE + 2 * r] = (uint8_t)(bits & 0xFF);",
                             "data[ORC_DNOPE + 2 * r] = (uint8_t)(bits >> 8);"),
+    "s_q_ignored": ("const int32_t seq = d->s_q > 1 ? b / d->s_q : b;",
+                    "const int32_t seq = b;"),
+    "s_q_table_only": ("valid[p] = (unsigned char)orc_resolve(d, J->bt, seq, idx, &page, &off);",
+                       "valid[p] = (unsigned char)orc_resolve(d, J->bt, b, idx, &page, &off);"),
     "dot_skips_rope": ("for (j = 0; j < ORC_D; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];",
                        "for (j = 0; j < 448; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];"),
 }
