@@ -85,7 +85,7 @@ const char* dsv4_last_error(void);
 #define DSV4_DECODE_SCRUB 0x1u
 
 typedef struct dsv4_decode_desc {
-    int32_t batch;               /* B: query tokens, one per sequence (s_q = 1), >= 1 */
+    int32_t batch;               /* B: query tokens (rows of q / topk_idx / out), >= 1 */
     int32_t num_heads;           /* H: multiple of 16 in [16, 128]                   */
     int32_t topk;                /* main entries per token, >= 0                     */
     int32_t swa;                 /* sliding-window entries per token, >= 0           */
@@ -97,6 +97,8 @@ typedef struct dsv4_decode_desc {
     int64_t topk_idx_stride;     /* elements between topk_idx rows; 0 = topk + swa   */
     float sm_scale;              /* multiplies q.k (never the sink)                  */
     uint32_t flags;              /* DSV4_DECODE_* bits; 0 = none                     */
+    int32_t tokens_per_seq;      /* s_q: query tokens per sequence (0 or 1 = one);
+                                    batch must be a multiple of it                   */
     void* workspace;             /* device scratch for split partials (may be NULL
                                     when the call needs none)                        */
     size_t workspace_bytes;      /* its size                                         */
@@ -138,12 +140,17 @@ size_t dsv4_sparse_decode_workspace_bytes(const dsv4_decode_desc* desc, int32_t 
 
 /* Sparse FP8 MLA decode with an attention sink.
  *
+ * Query token b belongs to sequence r = b / s_q (s_q = tokens_per_seq, 1
+ * when 0): the s_q tokens of a sequence (multi-token / MTP decode) each
+ * have their own q and topk_idx rows and share the sequence's block-table
+ * row and valid_len entry.  (SGLang PR #26208 report, gather+dequant
+ * kernel: the top-k length of token t is read at t // s_q.)
  * For token b and head h, entry k of topk_idx row b (columns [0, topk) are
  * the main list, [topk, topk+swa) the sliding window) takes part iff
  *   idx = topk_idx[b, k] >= 0, and
- *   k >= topk, or valid_len is NULL, or k < clamp(valid_len[b], 0, topk), and
+ *   k >= topk, or valid_len is NULL, or k < clamp(valid_len[r], 0, topk), and
  *   its page resolves: with a block table, idx/block_size <
- *   max_blocks_per_seq and page = block_table[b, idx/block_size] lies in
+ *   max_blocks_per_seq and page = block_table[r, idx/block_size] lies in
  *   [0, num_blocks); without one (block_table NULL), idx is a pool slot and
  *   page = idx/block_size must be < num_blocks.  The offset is idx%block_size.
  * With v_k the dequantised 512-wide row and s_k = sm_scale * q[b,h,:].v_k:
@@ -162,9 +169,9 @@ size_t dsv4_sparse_decode_workspace_bytes(const dsv4_decode_desc* desc, int32_t 
  *   q          bf16 [B, H, 512], contiguous, 16-byte aligned; q[...,j]
  *              pairs with row dim j (448 NoPE then 64 RoPE)
  *   kv_cache   uint8 [num_blocks, page_stride], 8-byte aligned
- *   block_table int32 [B, block_table_stride] or NULL
+ *   block_table int32 [B / s_q, block_table_stride] or NULL
  *   topk_idx   int32 [B, topk_idx_stride], columns [0, topk+swa) used
- *   valid_len  int32 [B] or NULL
+ *   valid_len  int32 [B / s_q] or NULL
  *   sink       float [H] or NULL
  *   out        bf16 [B, H, 512], contiguous, 16-byte aligned
  *   lse        float [B, H] or NULL (not written)

@@ -49,6 +49,7 @@ class dsv4_decode_desc(ctypes.Structure):
         ("topk_idx_stride", ctypes.c_int64),
         ("sm_scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+        ("tokens_per_seq", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -136,7 +137,8 @@ def _stream(stream) -> ctypes.c_void_p:
 def make_desc(*, batch: int, num_heads: int, topk: int, swa: int, block_size: int,
               num_blocks: int, page_stride: int, sm_scale: float, max_blocks_per_seq: int = 0,
               block_table_stride: int = 0, topk_idx_stride: int = 0,
-              workspace: Optional[torch.Tensor] = None, flags: int = 0) -> dsv4_decode_desc:
+              workspace: Optional[torch.Tensor] = None, flags: int = 0,
+              tokens_per_seq: int = 1) -> dsv4_decode_desc:
     d = dsv4_decode_desc()
     d.batch, d.num_heads, d.topk, d.swa = batch, num_heads, topk, swa
     d.block_size, d.max_blocks_per_seq = block_size, max_blocks_per_seq
@@ -144,6 +146,7 @@ def make_desc(*, batch: int, num_heads: int, topk: int, swa: int, block_size: in
     d.topk_idx_stride = topk_idx_stride
     d.sm_scale = sm_scale
     d.flags = flags
+    d.tokens_per_seq = tokens_per_seq
     if workspace is not None:
         d.workspace = workspace.data_ptr()
         d.workspace_bytes = workspace.numel() * workspace.element_size()

@@ -70,6 +70,10 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
                     (long long)d->block_size * kRowBytes, (long long)d->page_stride);
     if (d->num_blocks > INT64_MAX / d->page_stride)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "num_blocks * page_stride overflows");
+    if (d->tokens_per_seq < 0 || (d->tokens_per_seq > 1 && d->batch % d->tokens_per_seq))
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "tokens_per_seq must be >= 0 and divide batch (got %d for batch %d)",
+                    d->tokens_per_seq, d->batch);
     if (d->flags & ~DSV4_DECODE_SCRUB)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "unknown decode flags 0x%x",
                     (unsigned)(d->flags & ~DSV4_DECODE_SCRUB));
@@ -189,6 +193,7 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.max_blocks = bt ? d->max_blocks_per_seq : 0;
     p.S = sh.splits;
     p.G = sh.groups;
+    p.sq = d->tokens_per_seq > 1 ? d->tokens_per_seq : 1;
     p.qk_scale_log2 = d->sm_scale * 1.4426950408889634f;
     return p;
 }

@@ -214,12 +214,12 @@ __device__ __forceinline__ int32_t load_index(const DecodeParams& p, int b, int 
     return in ? v : -1;
 }
 
-__device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, int b, int32_t idx) {
+__device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, int seq, int32_t idx) {
     const bool ok = idx >= 0;
     const int64_t blk = (ok ? idx : 0) / p.bs;
     if (p.bt) {
         const bool inb = ok && blk < p.max_blocks;
-        const int32_t pg = p.bt[(int64_t)b * p.bt_stride + (inb ? blk : 0)];
+        const int32_t pg = p.bt[(int64_t)seq * p.bt_stride + (inb ? blk : 0)];
         return (inb && pg >= 0 && pg < p.num_blocks) ? pg : -1;
     }
     return (ok && blk < p.num_blocks) ? blk : -1;
@@ -288,11 +288,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     if (unit >= p.units) return;
     const int b = (int)(unit / p.S);
     const int s = (int)(unit % p.S);
+    const int seq = b / p.sq;                 // tokens of one sequence share its table and length
     const int h0 = g * HG;
 
     // This split's slice of the effective list main[0:vl] ++ swa, in chunks
     // rounded up to whole tiles.
-    const int vl = p.valid_len ? min(max(p.valid_len[b], 0), p.topk) : p.topk;
+    const int vl = p.valid_len ? min(max(p.valid_len[seq], 0), p.topk) : p.topk;
     const int eff = vl + p.swa;
     int chunk = (eff + p.S - 1) / p.S;
     chunk = (chunk + kTile - 1) / kTile * kTile;
@@ -335,8 +336,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     {
         const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
         const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
-        const int64_t g0 = lookup_page(p, b, i0);
-        const int64_t g1 = lookup_page(p, b, i1);
+        const int64_t g0 = lookup_page(p, seq, i0);
+        const int64_t g1 = lookup_page(p, seq, i1);
         write_meta(p, meta + 2 * tid, g0, i0);
         write_meta(p, meta + 2 * (kThreads + tid), g1, i1);
         const uint64_t b0 = __builtin_amdgcn_ballot_w64(g0 >= 0);
@@ -406,8 +407,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             r_i0 = e0 < hi ? r_i0 : -1;
             r_i1 = e0 + 64 < hi ? r_i1 : -1;
             if (p.bt) {
-                r_p0 = p.bt[(int64_t)b * p.bt_stride + bt_col(r_i0)];
-                r_p1 = p.bt[(int64_t)b * p.bt_stride + bt_col(r_i1)];
+                r_p0 = p.bt[(int64_t)seq * p.bt_stride + bt_col(r_i0)];
+                r_p1 = p.bt[(int64_t)seq * p.bt_stride + bt_col(r_i1)];
             }
         } else {
             const int64_t pg0 = page_of(r_i0, r_p0), pg1 = page_of(r_i1, r_p1);
@@ -751,7 +752,8 @@ __global__ __launch_bounds__(kThreads) void gather_floor_kernel(const DecodePara
     if (unit >= p.units) return;
     const int b = (int)(unit / p.S);
     const int s = (int)(unit % p.S);
-    const int vl = p.valid_len ? min(max(p.valid_len[b], 0), p.topk) : p.topk;
+    const int seq = b / p.sq;
+    const int vl = p.valid_len ? min(max(p.valid_len[seq], 0), p.topk) : p.topk;
     const int eff = vl + p.swa;
     int chunk = (eff + p.S - 1) / p.S;
     chunk = (chunk + kTile - 1) / kTile * kTile;
@@ -765,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void gather_floor_kernel(const DecodePara
         for (int e = 0; e < 2; ++e) {
             const int i = tid + e * kThreads;
             const int32_t id = load_index(p, b, vl, hi, base + i);
-            const int64_t pg = lookup_page(p, b, id);
+            const int64_t pg = lookup_page(p, seq, id);
             const uint8_t* pgp = p.kv + pg * p.page_stride;
             const int64_t off = id % p.bs;
             addr[i][0] = reinterpret_cast<int64_t>(pg >= 0 ? pgp + off * kRowData : kZeroRow);

@@ -63,9 +63,9 @@ constexpr size_t lds_bytes_for(int hg) {
 struct DecodeParams {
     const uint16_t* q;          // bf16 [B, H, 512]
     const uint8_t* kv;          // pages
-    const int32_t* bt;          // [B, bt_stride] or null
+    const int32_t* bt;          // [B / sq, bt_stride] or null
     const int32_t* idx;         // [B, idx_stride]
-    const int32_t* valid_len;   // [B] or null
+    const int32_t* valid_len;   // [B / sq] or null
     const float* sink;          // [H] or null
     uint16_t* out;              // bf16 [B, H, 512] (direct output, S == 1)
     float* lse;                 // [B, H] or null (direct output, S == 1)
@@ -77,6 +77,7 @@ struct DecodeParams {
     int64_t idx_stride;
     int64_t units;              // B * S
     int32_t B, H, topk, swa, bs, max_blocks, S, G;
+    int32_t sq;                 // query tokens per sequence (block-table row / valid_len entry)
     float qk_scale_log2;        // sm_scale * log2(e)
 };
 

@@ -44,7 +44,7 @@ def make_desc(w, *, use_bt=True, workspace=None, flags=0):
                           page_stride=w.page_stride, sm_scale=w.sm_scale,
                           max_blocks_per_seq=w.max_blocks_per_seq if use_bt else 0,
                           block_table_stride=w.block_table.shape[1] if use_bt else 0,
-                          workspace=workspace, flags=flags)
+                          workspace=workspace, flags=flags, tokens_per_seq=w.s_q)
 
 
 def gpu_decode(dw: DeviceWorkload, *, num_splits=None, use_bt=True, topk_idx=None,

@@ -67,6 +67,14 @@ def test_binding_structs_match_the_c_layout(struct, tmp_path):
     assert got == want
 
 
+def test_tokens_per_seq_must_divide_the_batch():
+    dsv4.dsv4_sparse_decode_plan(_desc(6, 64, 10, 0, tokens_per_seq=3))
+    dsv4.dsv4_sparse_decode_plan(_desc(6, 64, 10, 0, tokens_per_seq=0))
+    assert _status(_desc(6, 64, 10, 0, tokens_per_seq=4)) == dsv4.DSV4_ERR_INVALID_ARGUMENT
+    assert "tokens_per_seq" in dsv4.dsv4_last_error()
+    assert _status(_desc(6, 64, 10, 0, tokens_per_seq=-1)) == dsv4.DSV4_ERR_INVALID_ARGUMENT
+
+
 def test_unknown_decode_flags_are_rejected():
     dsv4.dsv4_sparse_decode_plan(_desc(1, 64, 10, 0, flags=dsv4.DSV4_DECODE_SCRUB))
     assert _status(_desc(1, 64, 10, 0, flags=0x2)) == dsv4.DSV4_ERR_INVALID_ARGUMENT
