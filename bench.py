@@ -59,6 +59,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to defeat the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-two-kernel", action="store_true",
+                    help="skip the fused vs two-kernel comparison on the large-batch workload")
     ap.add_argument("--scrub", action="store_true",
                     help="decode with the scrub flag (non-finite cache elements read as 0)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -336,10 +338,99 @@ def main() -> int:
         "kernel_source_digest": digest,
     }
 
+    if not args.no_two_kernel:
+        rec["two_kernel_large_batch"] = two_kernel_leg(dev, capture_fn=None)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, out, lse, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def two_kernel_leg(dev, capture_fn=None, K=50):
+    """Fused decode against the two-kernel path (gather + dequantise into
+    dense bf16 rows, then attention over them) on the large-batch workload
+    (B=256, H=64, top-k 512 + SWA 128, 8192 slots per sequence): average
+    launch durations from HIP graphs of K launches each, the cache rotated
+    over replicas so that every launch reads its rows from HBM."""
+    import torch
+    import sparse_mla_attention_block_amd as dsv4
+    from synth import make_workload
+    w = make_workload(3)
+    B, H, Kt = w.B, w.H, w.Kt
+    nb, stride = w.num_blocks, w.page_stride
+    n_valid = int((w.topk_idx >= 0).sum())
+    R = max(1, math.ceil(2 * INFINITY_CACHE_BYTES / (n_valid * (ROW_BYTES + 64))))
+    base = torch.from_numpy(w.kv).to(dev)
+    pool = torch.empty((R, nb, stride), dtype=torch.uint8, device=dev)
+    pool.copy_(base.unsqueeze(0).expand(R, nb, stride))
+    del base
+    bt0 = torch.from_numpy(w.block_table.astype(np.int64)).to(dev)
+    bts = [torch.where(bt0 >= 0, bt0 + r * nb, -1).to(torch.int32).contiguous() for r in range(R)]
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    sink = torch.from_numpy(w.sink).to(dev)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    dense = torch.empty((B, Kt, 512), dtype=torch.bfloat16, device=dev)
+    mask = torch.empty((B, Kt), dtype=torch.uint8, device=dev)
+    desc = dsv4.make_desc(batch=B, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
+                          num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale,
+                          max_blocks_per_seq=w.max_blocks_per_seq,
+                          block_table_stride=w.block_table.shape[1])
+    plan = dsv4.dsv4_sparse_decode_plan(desc, 0)
+    assert plan.num_splits == 1            # no split-K at >= 256 tokens: no workspace
+    kv = pool.view(-1)
+
+    def fused(r):
+        dsv4.dsv4_sparse_decode(desc, q, kv, bts[r], idx, None, sink, out, lse, 0)
+
+    def gather(r):
+        dsv4.dsv4_gather_dequant(desc, kv, bts[r], idx, None, dense, mask)
+
+    def attend(r):
+        dsv4.dsv4_dense_decode(desc, q, dense, mask, sink, out, lse, 0)
+
+    def timed(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                fn(i % R)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K * 1e3
+
+    t_fused = timed(fused)
+    fused_out = out.clone()
+    t_gather = timed(gather)
+    t_attend = timed(attend)
+    gather(0)
+    attend(0)
+    torch.cuda.synchronize()
+    diff = (out.float() - fused_out.float()).abs().max().item()
+    kv_bytes = n_valid * (ROW_BYTES + INDEX_BYTES)
+    dense_bytes = B * Kt * (1024 + 1)
+    return {
+        "workload": "large_batch: B=256 H=64 topk=512 swa=128, 8192 slots/seq, block 64",
+        "replicas": R, "launches": K,
+        "fused_us": t_fused, "gather_us": t_gather, "dense_attention_us": t_attend,
+        "two_kernel_us": t_gather + t_attend,
+        "fused_speedup": (t_gather + t_attend) / t_fused,
+        "fused_GBps": kv_bytes / (t_fused * 1e-6) / 1e9,
+        "gather_GBps": (kv_bytes + dense_bytes) / (t_gather * 1e-6) / 1e9,
+        "dense_attention_GBps": dense_bytes / (t_attend * 1e-6) / 1e9,
+        "max_abs_out_diff_vs_fused": diff,
+    }
 
 
 def cpu_baseline(w, out_gpu, lse_gpu, seconds):

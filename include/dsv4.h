@@ -216,6 +216,39 @@ int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
                         const void* part_out, const float* part_lse, const float* sink,
                         void* out, float* lse, hipStream_t stream);
 
+/* -------------------------------------------------- two-kernel path */
+
+/* The two-kernel decode: gather + dequantise into a dense bf16 buffer, then
+ * attention over it.  Results equal dsv4_sparse_decode's up to rounding (the
+ * same bf16 rows enter the same products); the fused call moves about 2.7x
+ * fewer bytes and is the production path.  (SGLang PR #26208 report: the
+ * gather+dequant kernel writing bf16 KV plus a mask, then the unified sparse
+ * attention kernel over it; SGLang PR #26383 page, implementation item 3:
+ * the fused kernel against this separate path.)
+ *
+ * Stage 1.  For every token b and column k of its topk_idx row, writes the
+ * dequantised row (448 NoPE then 64 RoPE values, bf16) to
+ * kv_out[b, k, :] and mask_out[b, k] = 0 when the entry takes part under
+ * the rules of dsv4_sparse_decode, else 1 with a zero row.  desc->flags may
+ * hold DSV4_DECODE_SCRUB (non-finite elements written as 0).
+ *   kv_out   bf16 [B, topk+swa, 512], 16-byte aligned
+ *   mask_out uint8 [B, topk+swa]
+ * Other arguments as for dsv4_sparse_decode (q and sink are not needed). */
+int dsv4_gather_dequant(const dsv4_decode_desc* desc, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* topk_idx,
+                        const int32_t* valid_len, void* kv_out, uint8_t* mask_out,
+                        hipStream_t stream);
+
+/* Stage 2.  Attention with the sink over kv_dense [B, topk+swa, 512] bf16
+ * (16-byte aligned) where entry k of token b takes part iff mask[b, k] == 0;
+ * out, lse, num_splits and the workspace as for dsv4_sparse_decode (the
+ * splits cover all topk+swa entries).  Only batch, num_heads, topk, swa,
+ * sm_scale and the workspace fields of desc are used (the cache geometry
+ * must still be valid); desc->flags must be 0. */
+int dsv4_dense_decode(const dsv4_decode_desc* desc, const void* q, const void* kv_dense,
+                      const uint8_t* mask, const float* sink, void* out, float* lse,
+                      int32_t num_splits, hipStream_t stream);
+
 /* ------------------------------------------------------ cache writer */
 
 /* Store flag: sanitise while quantising (see dsv4_quantize_store). */

@@ -96,6 +96,10 @@ _lib.dsv4_convert_req_index_to_global.argtypes = [
 _lib.dsv4_convert_req_index_to_global.restype = ctypes.c_int
 _lib.dsv4_gather_floor.argtypes = [_DESC, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
 _lib.dsv4_gather_floor.restype = ctypes.c_int
+_lib.dsv4_gather_dequant.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P]
+_lib.dsv4_gather_dequant.restype = ctypes.c_int
+_lib.dsv4_dense_decode.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]
+_lib.dsv4_dense_decode.restype = ctypes.c_int
 _lib.dsv4_quantize_store.argtypes = [_P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int32,
                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, _P]
 _lib.dsv4_quantize_store.restype = ctypes.c_int
@@ -201,6 +205,21 @@ def dsv4_convert_req_index_to_global(req_id: Optional[torch.Tensor], num_reqs: i
         _ptr(req_id), num_reqs, _ptr(block_table), bt_stride, max_blocks_per_req,
         _ptr(token_indices), ti_stride, num_tokens, width, block_size, _ptr(cu_seqlens),
         invalid_fill, _ptr(out), _stream(stream)))
+
+
+def dsv4_gather_dequant(desc, kv_cache: torch.Tensor, block_table: Optional[torch.Tensor],
+                        topk_idx: torch.Tensor, valid_len: Optional[torch.Tensor],
+                        kv_out: torch.Tensor, mask_out: torch.Tensor, stream=None) -> None:
+    _check(_lib.dsv4_gather_dequant(ctypes.byref(desc), _ptr(kv_cache), _ptr(block_table),
+                                    _ptr(topk_idx), _ptr(valid_len), _ptr(kv_out), _ptr(mask_out),
+                                    _stream(stream)))
+
+
+def dsv4_dense_decode(desc, q: torch.Tensor, kv_dense: torch.Tensor, mask: torch.Tensor,
+                      sink: Optional[torch.Tensor], out: torch.Tensor, lse: Optional[torch.Tensor],
+                      num_splits: int = 0, stream=None) -> None:
+    _check(_lib.dsv4_dense_decode(ctypes.byref(desc), _ptr(q), _ptr(kv_dense), _ptr(mask),
+                                  _ptr(sink), _ptr(out), _ptr(lse), num_splits, _stream(stream)))
 
 
 def dsv4_quantize_store(rows: torch.Tensor, row_stride: int, slot_mapping: torch.Tensor,

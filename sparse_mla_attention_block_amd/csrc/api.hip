@@ -172,6 +172,7 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.bt = bt;
     p.idx = idx;
     p.valid_len = valid_len;
+    p.mask = nullptr;
     p.sink = sink;
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
@@ -361,6 +362,77 @@ int dsv4_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
     p.fill = invalid_fill;
     (void)hipGetLastError();
     return launched(dsv4::launch_convert(p, stream), "convert");
+}
+
+int dsv4_gather_dequant(const dsv4_decode_desc* desc, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* topk_idx,
+                        const int32_t* valid_len, void* kv_out, uint8_t* mask_out,
+                        hipStream_t stream) {
+    Shape sh;
+    dsv4_plan plan;
+    int st = make_plan(desc, 1, &sh, &plan);
+    if (st) return st;
+    if (!kv_cache || !topk_idx || !kv_out || !mask_out)
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "kv_cache, topk_idx, kv_out and mask_out must not be NULL");
+    if (!aligned(kv_cache, 8)) return fail(DSV4_ERR_INVALID_ARGUMENT, "kv_cache must be 8-byte aligned");
+    if (!aligned(kv_out, 16)) return fail(DSV4_ERR_INVALID_ARGUMENT, "kv_out must be 16-byte aligned");
+    if (block_table && (desc->max_blocks_per_seq < 1 ||
+                        desc->block_table_stride < desc->max_blocks_per_seq))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "bad block-table geometry");
+    if ((int64_t)desc->batch * ((sh.kt + dsv4::kTile - 1) / dsv4::kTile) > INT32_MAX)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "batch * entries too large");
+    dsv4::DecodeParams p = make_params(desc, sh, nullptr, kv_cache, block_table, topk_idx,
+                                       valid_len, nullptr, nullptr, nullptr);
+    (void)hipGetLastError();
+    return launched(dsv4::launch_gather_dequant(p, static_cast<uint16_t*>(kv_out), mask_out,
+                                                (desc->flags & DSV4_DECODE_SCRUB) != 0, stream),
+                    "gather dequant");
+}
+
+int dsv4_dense_decode(const dsv4_decode_desc* desc, const void* q, const void* kv_dense,
+                      const uint8_t* mask, const float* sink, void* out, float* lse,
+                      int32_t num_splits, hipStream_t stream) {
+    Shape sh;
+    dsv4_plan plan;
+    int st = make_plan(desc, num_splits, &sh, &plan);
+    if (st) return st;
+    if (desc->flags)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "dense decode takes no flags (scrub applies when "
+                                               "gathering)");
+    if (!q || !kv_dense || !mask || !out)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "q, kv_dense, mask and out must not be NULL");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(kv_dense, 16))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "q, kv_dense and out must be 16-byte aligned");
+    if (plan.workspace_bytes) {
+        if (!desc->workspace || desc->workspace_bytes < plan.workspace_bytes)
+            return fail(DSV4_ERR_WORKSPACE_TOO_SMALL, "num_splits = %d needs a workspace of %zu bytes",
+                        plan.num_splits, plan.workspace_bytes);
+        if (!aligned(desc->workspace, 16))
+            return fail(DSV4_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    }
+    // Dense rows: every token has kt entries, all in one effective list.
+    dsv4::DecodeParams p = make_params(desc, sh, q, kv_dense, nullptr, nullptr, nullptr, sink, out,
+                                       lse);
+    p.mask = mask;
+    p.topk = (int32_t)sh.kt;
+    p.swa = 0;
+    p.idx_stride = sh.kt;
+    p.sq = 1;
+    p.max_blocks = 0;
+    (void)hipGetLastError();
+    st = launched(dsv4::launch_dense_partial(p, sh.hg, plan.grid_partial, stream), "dense partial");
+    if (st || sh.splits == 1) return st;
+    dsv4::CombineParams c;
+    c.part_o = p.part_o;
+    c.part_lse = p.part_lse;
+    c.sink = sink;
+    c.out = p.out;
+    c.lse = lse;
+    c.B = desc->batch;
+    c.H = desc->num_heads;
+    c.S = sh.splits;
+    return launched(dsv4::launch_combine(c, stream), "combine");
 }
 
 int dsv4_quantize_store(const void* rows, int64_t row_stride, const int64_t* slot_mapping,

@@ -81,9 +81,11 @@ __device__ __forceinline__ bf16x8 dequant8(uint2 raw, uint32_t code) {
 }
 
 // Source of rows that take no part and of tiles past the end of a split: 576
-// zero data bytes and a zero scale word, which dequantise to exact zeros, so
-// a NaN anywhere in the cache can never reach an MFMA.
-__device__ __attribute__((aligned(64))) const uint8_t kZeroRow[kRowData + 64] = {};
+// zero data bytes and a zero scale word, which dequantise to exact zeros, or
+// a whole zero bf16 row (1024 bytes) for dense sources, so a NaN anywhere in
+// the cache can never reach an MFMA.
+constexpr int kDenseRow = kD * 2;
+__device__ __attribute__((aligned(64))) const uint8_t kZeroRow[kDenseRow] = {};
 
 // Reductions over the 16 lanes of a DPP row (lanes sharing lane >> 4):
 // quad xor 1, quad xor 2, half-row mirror, row mirror.
@@ -202,6 +204,53 @@ __device__ __forceinline__ void store_patch(const uint32_t (&rr)[64], int prow, 
     }
 }
 
+// Dense bf16 source (the two-kernel path's gathered rows): lane l8 of a row
+// holds its 16-byte units 8j + l8, j = 0..7 (32 registers per tile), stored
+// into the K tile exactly where the FP8 path stores its dequantised units.
+typedef const __attribute__((address_space(1))) u32x4 gu32x4;
+
+__device__ __forceinline__ gbyte* dense_src(const int64_t* meta, int prow, bool live) {
+    const int64_t m = meta[2 * prow];
+    return (gbyte*)(live ? m : reinterpret_cast<int64_t>(kZeroRow));
+}
+
+template <int O>
+__device__ __forceinline__ void load_dense(gbyte* src, int l8, uint32_t (&rr)[64]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const u32x4 v = *(gu32x4*)(src + 128 * j + 16 * l8);
+        rr[O + 4 * j] = v[0];
+        rr[O + 4 * j + 1] = v[1];
+        rr[O + 4 * j + 2] = v[2];
+        rr[O + 4 * j + 3] = v[3];
+    }
+}
+
+template <int O>
+__device__ __forceinline__ void store_dense(const uint32_t (&rr)[64], int prow, int l8,
+                                            __bf16* Kt) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<u32x4*>(Kt + kofs(prow, 64 * j + 8 * l8)) =
+            u32x4{rr[O + 4 * j], rr[O + 4 * j + 1], rr[O + 4 * j + 2], rr[O + 4 * j + 3]};
+}
+
+// A dense entry: row `pos` of token b's gathered rows takes part when it
+// lies in [lo, hi) and its mask byte is 0.  The mask load is unconditional
+// (an out-of-range position reads the split's first entry).
+__device__ __forceinline__ bool dense_live(const DecodeParams& p, int b, int lo, int hi, int pos) {
+    const int col = pos < hi ? pos : lo;
+    const uint8_t m = p.mask[(int64_t)b * p.idx_stride + col];
+    return pos < hi && m == 0;
+}
+
+__device__ __forceinline__ void write_dense_meta(const DecodeParams& p, int64_t* row, int b,
+                                                 int pos, bool live) {
+    const uint8_t* r = p.kv + ((int64_t)b * p.idx_stride + pos) * kDenseRow;
+    row[0] = reinterpret_cast<int64_t>(live ? r : kZeroRow);
+    row[1] = 0;
+}
+
 // Entry resolution helpers: effective position -> index -> page.  Both loads
 // are unconditional (an out-of-range position reads column 0, a masked index
 // block 0 of the row's table) and the result is selected afterwards, so the
@@ -259,8 +308,11 @@ __device__ __forceinline__ float xrow_sum4(float v) {
     return xrow4(v, [](float p, float q) { return p + q; });
 }
 
-template <int HG, bool SCRUB>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
+// The partial kernel's body.  SCRUB: non-finite dequantised elements read
+// as 0.  DENSE: rows come from a gathered bf16 buffer [B, idx_stride, 512]
+// with a per-entry mask (1 = takes no part) instead of the FP8 cache.
+template <int HG, bool SCRUB, bool DENSE>
+__device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     constexpr int MT = HG / 16;              // 16-head MFMA tiles; consumer wave w owns tile w
     static_assert(HG % 16 == 0 && HG <= kMaxHeadsPerGroup, "head group");
     using L = Smem<HG>;
@@ -334,14 +386,24 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // covers tiles 2w, 2w+1 and 16+2w, 17+2w).  Later tiles are resolved 16 at
     // a time inside the loop, which only splits longer than 32 tiles reach.
     {
-        const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
-        const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
-        const int64_t g0 = lookup_page(p, seq, i0);
-        const int64_t g1 = lookup_page(p, seq, i1);
-        write_meta(p, meta + 2 * tid, g0, i0);
-        write_meta(p, meta + 2 * (kThreads + tid), g1, i1);
-        const uint64_t b0 = __builtin_amdgcn_ballot_w64(g0 >= 0);
-        const uint64_t b1 = __builtin_amdgcn_ballot_w64(g1 >= 0);
+        uint64_t b0, b1;
+        if constexpr (DENSE) {
+            const bool v0 = dense_live(p, b, lo, hi, lo + tid);
+            const bool v1 = dense_live(p, b, lo, hi, lo + kThreads + tid);
+            write_dense_meta(p, meta + 2 * tid, b, lo + tid, v0);
+            write_dense_meta(p, meta + 2 * (kThreads + tid), b, lo + kThreads + tid, v1);
+            b0 = __builtin_amdgcn_ballot_w64(v0);
+            b1 = __builtin_amdgcn_ballot_w64(v1);
+        } else {
+            const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
+            const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
+            const int64_t g0 = lookup_page(p, seq, i0);
+            const int64_t g1 = lookup_page(p, seq, i1);
+            write_meta(p, meta + 2 * tid, g0, i0);
+            write_meta(p, meta + 2 * (kThreads + tid), g1, i1);
+            b0 = __builtin_amdgcn_ballot_w64(g0 >= 0);
+            b1 = __builtin_amdgcn_ballot_w64(g1 >= 0);
+        }
         if (lane == 0) {
             vmask[2 * wave] = (uint32_t)b0;
             vmask[2 * wave + 1] = (uint32_t)(b0 >> 32);
@@ -352,12 +414,20 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     __syncthreads();
 
     if (producer) {
-        load_patch<0>(patch_src(meta_tile(0), prow, ntiles > 0), l8, rr);
-        load_patch<20>(patch_src(meta_tile(1), prow, ntiles > 1), l8, rr);
-        load_patch<40>(patch_src(meta_tile(2), prow, ntiles > 2), l8, rr);
-        const PatchSrc a3 = patch_src(meta_tile(3), prow, ntiles > 3);
-        store_patch<0, SCRUB>(rr, prow, l8, kbuf(0));
-        load_patch<0>(a3, l8, rr);
+        if constexpr (DENSE) {
+            load_dense<0>(dense_src(meta_tile(0), prow, ntiles > 0), l8, rr);
+            load_dense<32>(dense_src(meta_tile(1), prow, ntiles > 1), l8, rr);
+            gbyte* a2 = dense_src(meta_tile(2), prow, ntiles > 2);
+            store_dense<0>(rr, prow, l8, kbuf(0));
+            load_dense<0>(a2, l8, rr);
+        } else {
+            load_patch<0>(patch_src(meta_tile(0), prow, ntiles > 0), l8, rr);
+            load_patch<20>(patch_src(meta_tile(1), prow, ntiles > 1), l8, rr);
+            load_patch<40>(patch_src(meta_tile(2), prow, ntiles > 2), l8, rr);
+            const PatchSrc a3 = patch_src(meta_tile(3), prow, ntiles > 3);
+            store_patch<0, SCRUB>(rr, prow, l8, kbuf(0));
+            load_patch<0>(a3, l8, rr);
+        }
     }
     __syncthreads();
 
@@ -400,6 +470,27 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         const int nxt = t - ph + kHalfTiles;      // first tile of the next half
         if (nxt < kMetaTiles || nxt >= ntiles || ph >= 3) return;
         const int e0 = lo + nxt * kTile + 128 * wave + lane;
+        if constexpr (DENSE) {
+            // Phase 0 loads the two mask bytes, phase 2 publishes.
+            if (ph == 0) {
+                r_i0 = dense_live(p, b, lo, hi, e0);
+                r_i1 = dense_live(p, b, lo, hi, e0 + 64);
+            } else if (ph == 2) {
+                int64_t* m = meta_tile(nxt) + 2 * (128 * wave + lane);
+                write_dense_meta(p, m, b, e0, r_i0 != 0);
+                write_dense_meta(p, m + 2 * 64, b, e0 + 64, r_i1 != 0);
+                const uint64_t b0 = __builtin_amdgcn_ballot_w64(r_i0 != 0);
+                const uint64_t b1 = __builtin_amdgcn_ballot_w64(r_i1 != 0);
+                if (lane == 0) {
+                    uint32_t* vmk = vmask + (nxt + 4 * wave) % kMetaTiles;
+                    vmk[0] = (uint32_t)b0;
+                    vmk[1] = (uint32_t)(b0 >> 32);
+                    vmk[2] = (uint32_t)b1;
+                    vmk[3] = (uint32_t)(b1 >> 32);
+                }
+            }
+            return;
+        }
         if (ph == 0) {
             r_i0 = raw_index(e0);
             r_i1 = raw_index(e0 + 64);
@@ -593,10 +684,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
         }
     };
 
-    // Both loops run the same nsteps >= ntiles + 1 steps (a multiple of 3, the
-    // producers' unroll, so their loop body has no branch around a load);
-    // steps past ntiles do nothing but the barrier.
-    const int nsteps = (ntiles + 1 + 2) / 3 * 3;
+    // Both loops run the same nsteps >= ntiles + 1 steps (a multiple of the
+    // producers' unroll, 3 or 6 for dense rows, so their loop body has no
+    // branch around a load); steps past ntiles do nothing but the barrier.
+    constexpr int kUnroll = DENSE ? 6 : 3;
+    const int nsteps = (ntiles + kUnroll) / kUnroll * kUnroll;
     // Pipeline step t = 0..ntiles, then one barrier: QK + softmax of tile t
     // (consumers), PV of tile t-1 (all waves), dequantisation of tile t+1 and
     // loads of tile t+4 (producers), staged resolution of the next half
@@ -604,7 +696,30 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     // the same barriers, so the producers' loop holds no load but their own
     // and the compiler counts them exactly: storing tile t+1 waits for its
     // loads only, with tiles t+2 and t+3 still in flight.
-    if (producer) {
+    if (producer && DENSE) {
+        // Dense rows take 32 registers a tile, so two tiles are in flight:
+        // tile k lives in rr[32(k%2) .. +31]; step t stores tile t+1 into K
+        // buffer (t+1)%3 and reuses its registers for tile t+3 (period 6).
+        auto dstep = [&](int t, auto kset, auto rset) __attribute__((always_inline)) {
+            constexpr int O = 32 * decltype(rset)::value;
+            gbyte* a = dense_src(meta_tile(t + 3), prow, t + 3 < ntiles);
+            store_dense<O>(rr, prow, l8, Kn + decltype(kset)::value * (kTile * kD));
+            load_dense<O>(a, l8, rr);
+            if (t >= 1 && t <= ntiles) pv(t - 1);
+            __syncthreads();
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        for (int t = 0; t < nsteps; t += 6) {
+            dstep(t, I1{}, I1{});
+            dstep(t + 1, I2{}, I0{});
+            dstep(t + 2, I0{}, I1{});
+            dstep(t + 3, I1{}, I0{});
+            dstep(t + 4, I2{}, I1{});
+            dstep(t + 5, I0{}, I0{});
+        }
+    } else if (producer) {
         // Tile k's raw bytes live in rr[20(k%3) .. +19]; step t stores tile
         // t+1 into K buffer (t+1)%3 and reuses its registers for tile t+4.
         auto pstep = [&](int t, auto set) __attribute__((always_inline)) {
@@ -677,6 +792,63 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
             *reinterpret_cast<bf16x4*>(row + 16 * nt) = o;
         }
     }
+}
+
+template <int HG, bool SCRUB>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
+    decode_partial_body<HG, SCRUB, false>(p);
+}
+
+// Attention over gathered bf16 rows (second kernel of the two-kernel path).
+template <int HG>
+__global__ __launch_bounds__(kThreads) void dense_partial_kernel(const DecodeParams p) {
+    decode_partial_body<HG, false, true>(p);
+}
+
+// Two-kernel path, first kernel: gather and dequantise every entry of every
+// token's index row into a dense bf16 buffer [B, topk+swa, 512] (row k =
+// column k of the index row) with a mask byte per entry (1 = takes no part;
+// its row is written as zeros).  (SGLang PR #26208 report, the gather+dequant
+// kernel and its output mask.)  32 entries per workgroup, 8 lanes per entry,
+// the same row loads and dequantisation as the fused kernel's producers.
+template <bool SCRUB>
+__global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(const DecodeParams p,
+                                                                       uint16_t* kv_out,
+                                                                       uint8_t* mask_out) {
+    const int Kt = p.topk + p.swa;
+    const int tiles = (Kt + kTile - 1) / kTile;
+    const int b = (int)(blockIdx.x / tiles);
+    const int col = (int)(blockIdx.x % tiles) * kTile + (threadIdx.x >> 3);
+    const int l8 = threadIdx.x & 7;
+    if (col >= Kt) return;                         // no barrier in this kernel
+    const int seq = b / p.sq;
+    const int vl = p.valid_len ? min(max(p.valid_len[seq], 0), p.topk) : p.topk;
+    const int32_t raw = p.idx[(int64_t)b * p.idx_stride + col];
+    const int32_t idx = col < p.topk && col >= vl ? -1 : raw;
+    const int64_t page = lookup_page(p, seq, idx);
+    int64_t m[2];
+    write_meta(p, m, page, idx);
+    uint32_t rr[64];
+    load_patch<0>(PatchSrc{(gbyte*)m[0], (gbyte*)m[1]}, l8, rr);
+    uint16_t* dst = kv_out + ((int64_t)b * Kt + col) * kD;
+    const uint64_t sw = (uint64_t)rr[19] << 32 | rr[18];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+        bf16x8 v = dequant8(make_uint2(rr[2 * j], rr[2 * j + 1]), (uint32_t)(sw >> (8 * j)) & 0xFFu);
+        if (SCRUB) {
+            u32x4 w = __builtin_bit_cast(u32x4, v);
+            w = u32x4{scrub_pair(w[0]), scrub_pair(w[1]), scrub_pair(w[2]), scrub_pair(w[3])};
+            v = __builtin_bit_cast(bf16x8, w);
+        }
+        *reinterpret_cast<bf16x8*>(dst + 64 * j + 8 * l8) = v;
+    }
+#pragma unroll
+    for (int j = 7; j < kChunks; ++j) {
+        uint2 r = make_uint2(rr[2 * j], rr[2 * j + 1]);
+        if (SCRUB) r = make_uint2(scrub_pair(r.x), scrub_pair(r.y));
+        *reinterpret_cast<uint2*>(dst + kDNope + 32 * (j - 7) + 4 * l8) = r;
+    }
+    if (l8 == 0) mask_out[(int64_t)b * Kt + col] = page >= 0 ? 0 : 1;
 }
 
 // Merge of split partials with the sink; one workgroup per (token, head),
@@ -818,6 +990,31 @@ static hipError_t launch_partial_variant(const DecodeParams& p, int heads_per_gr
         case 64: hipLaunchKernelGGL((decode_partial_kernel<64, SCRUB>), g, blk, 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
+                                hipStream_t stream) {
+    const dim3 g((unsigned)grid), blk(kThreads);
+    switch (heads_per_group) {
+        case 16: hipLaunchKernelGGL(dense_partial_kernel<16>, g, blk, 0, stream, p); break;
+        case 32: hipLaunchKernelGGL(dense_partial_kernel<32>, g, blk, 0, stream, p); break;
+        case 48: hipLaunchKernelGGL(dense_partial_kernel<48>, g, blk, 0, stream, p); break;
+        case 64: hipLaunchKernelGGL(dense_partial_kernel<64>, g, blk, 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_dequant(const DecodeParams& p, uint16_t* kv_out, uint8_t* mask_out,
+                                 bool scrub, hipStream_t stream) {
+    const int64_t grid = (int64_t)p.B * ((p.topk + p.swa + kTile - 1) / kTile);
+    if (scrub)
+        hipLaunchKernelGGL(gather_dequant_kernel<true>, dim3((unsigned)grid), dim3(kGatherThreads),
+                           0, stream, p, kv_out, mask_out);
+    else
+        hipLaunchKernelGGL(gather_dequant_kernel<false>, dim3((unsigned)grid), dim3(kGatherThreads),
+                           0, stream, p, kv_out, mask_out);
     return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ constexpr int kMaxSplits = 64;
 constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin
 constexpr int kCombineThreads = 128;  // 4 output dims per thread
+constexpr int kGatherThreads = 256;   // two-kernel path gather: 32 entries x 8 lanes
 
 // LDS tile geometry.  K tiles are row-major [32][512] bf16 with the 16-byte
 // units of each row permuted (see the kernel); probabilities [HG][40] bf16.
@@ -66,6 +67,7 @@ struct DecodeParams {
     const int32_t* bt;          // [B / sq, bt_stride] or null
     const int32_t* idx;         // [B, idx_stride]
     const int32_t* valid_len;   // [B / sq] or null
+    const uint8_t* mask;        // dense source only: [B, idx_stride], 1 = no part
     const float* sink;          // [H] or null
     uint16_t* out;              // bf16 [B, H, 512] (direct output, S == 1)
     float* lse;                 // [B, H] or null (direct output, S == 1)
@@ -128,6 +130,10 @@ __device__ __forceinline__ uint32_t scrub_pair(uint32_t w) {
 
 // Kernel launchers (return the launch's hipError_t).
 hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
+                                 bool scrub, hipStream_t stream);
+hipError_t launch_dense_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
+                                hipStream_t stream);
+hipError_t launch_gather_dequant(const DecodeParams& p, uint16_t* kv_out, uint8_t* mask_out,
                                  bool scrub, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     for want in ("dsv4_sparse_decode", "dsv4_sparse_decode_partial", "dsv4_combine_splits",
                  "dsv4_convert_req_index_to_global", "dsv4_sparse_decode_plan",
                  "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error",
-                 "dsv4_gather_floor", "dsv4_quantize_store"):
+                 "dsv4_gather_floor", "dsv4_quantize_store", "dsv4_gather_dequant",
+                 "dsv4_dense_decode"):
         assert want in names
 
 
@@ -229,3 +230,18 @@ def test_writer_validation_without_touching_the_gpu():
     assert lib.dsv4_quantize_store(ctypes.c_void_p(4104), 512, fake, 4, fake, 64, 10, 64 * 584,
                                    S, None) == E          # rows misaligned
     assert lib.dsv4_quantize_store(fake, 512, fake, -1, fake, 64, 10, 64 * 584, S, None) == E
+
+
+def test_two_kernel_path_validation_without_touching_the_gpu():
+    lib = dsv4._lib
+    fake = ctypes.c_void_p(4096)
+    E = dsv4.DSV4_ERR_INVALID_ARGUMENT
+    d = _desc(2, 64, 100, 20)
+    assert lib.dsv4_gather_dequant(ctypes.byref(d), fake, None, fake, None, None, fake, None) == E
+    assert lib.dsv4_gather_dequant(ctypes.byref(d), fake, None, fake, None, ctypes.c_void_p(4104),
+                                   fake, None) == E                       # kv_out misaligned
+    assert lib.dsv4_dense_decode(ctypes.byref(d), fake, fake, None, None, fake, None, 1, None) == E
+    assert lib.dsv4_dense_decode(ctypes.byref(d), fake, fake, fake, None, fake, None, 4,
+                                 None) == dsv4.DSV4_ERR_WORKSPACE_TOO_SMALL
+    ds = _desc(2, 64, 100, 20, flags=dsv4.DSV4_DECODE_SCRUB)
+    assert lib.dsv4_dense_decode(ctypes.byref(ds), fake, fake, fake, None, fake, None, 1, None) == E
