@@ -295,3 +295,45 @@ def test_gather_floor_loads_exactly_the_taking_part_rows():
             sc = kv[pg, w.block_size * 576 + off * 8: w.block_size * 576 + off * 8 + 8]
             want ^= np.bitwise_xor.reduce(np.concatenate([data, sc]).view(np.uint32))
     assert got == want
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_very_long_index_list(S):
+    """16384 main entries: at S = 1 one workgroup walks 512 tiles, so the
+    32-tile resolution ring is refilled 30 times."""
+    w = make_custom(B=1, H=16, topk=16384, swa=64, seq_lens=[200000], seed=210 + S,
+                    invalid_frac=0.01)
+    _check(w, f"topk=16384 S={S}", num_splits=S)
+
+
+def test_many_tokens_with_short_lists():
+    rng = np.random.default_rng(220)
+    w = make_custom(B=2048, H=16, topk=32, swa=8, seq_lens=list(rng.integers(20, 200, 2048)),
+                    seed=220, invalid_frac=0.1, valid_len_range=(0, 32))
+    _check(w, "B=2048 short lists", num_splits=0)
+
+
+def test_block_size_128():
+    w = make_custom(B=3, H=32, topk=400, swa=40, seq_lens=[7000, 1300, 129], seed=230,
+                    block_size=128, invalid_frac=0.02, valid_len_range=(200, 400))
+    _check(w, "bs=128", num_splits=0)
+    _check(w, "bs=128 S=5", num_splits=5)
+
+
+def test_multi_token_over_global_slots():
+    """Without a block table the s_q tokens of a sequence still share its
+    top-k length."""
+    gh = _gh()
+    w = make_custom(B=3, H=32, topk=128, swa=16, seq_lens=[3000, 800, 300], seed=240, s_q=3,
+                    valid_len_range=(40, 128))
+    slots = np.where(w.topk_idx >= 0,
+                     w.block_table[np.arange(w.B)[:, None] // 3, np.maximum(w.topk_idx, 0)
+                                   // w.block_size] * w.block_size
+                     + np.maximum(w.topk_idx, 0) % w.block_size, -1).astype(np.int32)
+    dw = gh.DeviceWorkload(w)
+    print("multi-token global slots", flush=True)
+    out, lse = gh.gpu_decode(dw, num_splits=2, use_bt=False, topk_idx=torch.from_numpy(slots).cuda())
+    ro, rl, _ = oracle.decode_workload(w, topk_idx=slots, use_block_table=False, num_splits=2)
+    gh.assert_decode_close(out, lse, ro, rl, "multi-token global slots")
+    ro2, rl2, _ = oracle.decode_workload(w, num_splits=2)
+    gh.assert_decode_close(out, lse, ro2, rl2, "multi-token global slots vs block table")
