@@ -84,6 +84,18 @@ const char* dsv4_last_error(void);
  * the choice on a flag.)  Other bits are reserved and must be 0. */
 #define DSV4_DECODE_SCRUB 0x1u
 
+/* Provenance gate: the decode flags a cache of this provenance needs.
+ * Returns 0 (the scrub may be skipped) only when every condition holds:
+ * the cache is in the fp8_ds_mla format, no KV transfer (another engine,
+ * another process) wrote into it, the extra (compressed) cache is present,
+ * and its writer sanitised (dsv4_quantize_store with DSV4_STORE_SANITIZE,
+ * or an equivalent writer); otherwise DSV4_DECODE_SCRUB.  Host-only; never
+ * fails.  (vLLM PR #52212 page, implementation item 3 and the ROCm
+ * entry-layer snippet: the NaN-free trust gate, whose gfx950 clause stands
+ * for the sanitising writer that platform enables.) */
+uint32_t dsv4_decode_flags_for_cache(int32_t cache_is_fp8_ds_mla, int32_t has_kv_transfer,
+                                     int32_t has_extra_cache, int32_t writer_sanitizes);
+
 typedef struct dsv4_decode_desc {
     int32_t batch;               /* B: query tokens (rows of q / topk_idx / out), >= 1 */
     int32_t num_heads;           /* H: multiple of 16 in [16, 128]                   */

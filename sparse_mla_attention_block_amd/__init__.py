@@ -96,6 +96,8 @@ _lib.dsv4_convert_req_index_to_global.argtypes = [
 _lib.dsv4_convert_req_index_to_global.restype = ctypes.c_int
 _lib.dsv4_gather_floor.argtypes = [_DESC, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
 _lib.dsv4_gather_floor.restype = ctypes.c_int
+_lib.dsv4_decode_flags_for_cache.argtypes = [ctypes.c_int32] * 4
+_lib.dsv4_decode_flags_for_cache.restype = ctypes.c_uint32
 _lib.dsv4_gather_dequant.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P]
 _lib.dsv4_gather_dequant.restype = ctypes.c_int
 _lib.dsv4_dense_decode.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]
@@ -205,6 +207,12 @@ def dsv4_convert_req_index_to_global(req_id: Optional[torch.Tensor], num_reqs: i
         _ptr(req_id), num_reqs, _ptr(block_table), bt_stride, max_blocks_per_req,
         _ptr(token_indices), ti_stride, num_tokens, width, block_size, _ptr(cu_seqlens),
         invalid_fill, _ptr(out), _stream(stream)))
+
+
+def dsv4_decode_flags_for_cache(*, cache_is_fp8_ds_mla: bool, has_kv_transfer: bool,
+                                has_extra_cache: bool, writer_sanitizes: bool) -> int:
+    return int(_lib.dsv4_decode_flags_for_cache(int(cache_is_fp8_ds_mla), int(has_kv_transfer),
+                                                int(has_extra_cache), int(writer_sanitizes)))
 
 
 def dsv4_gather_dequant(desc, kv_cache: torch.Tensor, block_table: Optional[torch.Tensor],

@@ -364,6 +364,13 @@ int dsv4_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
     return launched(dsv4::launch_convert(p, stream), "convert");
 }
 
+uint32_t dsv4_decode_flags_for_cache(int32_t cache_is_fp8_ds_mla, int32_t has_kv_transfer,
+                                     int32_t has_extra_cache, int32_t writer_sanitizes) {
+    const bool trusted = cache_is_fp8_ds_mla && !has_kv_transfer && has_extra_cache &&
+                         writer_sanitizes;
+    return trusted ? 0u : DSV4_DECODE_SCRUB;
+}
+
 int dsv4_gather_dequant(const dsv4_decode_desc* desc, const void* kv_cache,
                         const int32_t* block_table, const int32_t* topk_idx,
                         const int32_t* valid_len, void* kv_out, uint8_t* mask_out,

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
                  "dsv4_convert_req_index_to_global", "dsv4_sparse_decode_plan",
                  "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error",
                  "dsv4_gather_floor", "dsv4_quantize_store", "dsv4_gather_dequant",
-                 "dsv4_dense_decode"):
+                 "dsv4_dense_decode", "dsv4_decode_flags_for_cache"):
         assert want in names
 
 
@@ -245,3 +245,15 @@ def test_two_kernel_path_validation_without_touching_the_gpu():
                                  None) == dsv4.DSV4_ERR_WORKSPACE_TOO_SMALL
     ds = _desc(2, 64, 100, 20, flags=dsv4.DSV4_DECODE_SCRUB)
     assert lib.dsv4_dense_decode(ctypes.byref(ds), fake, fake, fake, None, fake, None, 1, None) == E
+
+
+def test_provenance_gate_truth_table():
+    """The scrub may be skipped for exactly one of the 16 provenances: an
+    fp8_ds_mla cache with its extra cache, no KV transfer and a sanitising
+    writer."""
+    import itertools
+    for fmt, xfer, extra, san in itertools.product((False, True), repeat=4):
+        flags = dsv4.dsv4_decode_flags_for_cache(cache_is_fp8_ds_mla=fmt, has_kv_transfer=xfer,
+                                                 has_extra_cache=extra, writer_sanitizes=san)
+        trusted = fmt and not xfer and extra and san
+        assert flags == (0 if trusted else dsv4.DSV4_DECODE_SCRUB), (fmt, xfer, extra, san)
