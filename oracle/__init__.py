@@ -71,6 +71,10 @@ def lib():
         L.orc_sparse_decode.argtypes = [ctypes.POINTER(OrcDesc), P, P, P, P, P, P, ctypes.c_int32,
                                         P, P, ctypes.c_int32]
         L.orc_sparse_decode.restype = ctypes.c_int64
+        L.orc_sparse_decode_dual.argtypes = [ctypes.POINTER(OrcDesc), ctypes.POINTER(OrcDesc),
+                                             P, P, P, P, P, P, P, P, ctypes.c_int32, P, P,
+                                             ctypes.c_int32]
+        L.orc_sparse_decode_dual.restype = ctypes.c_int64
         L.orc_convert_req_index_to_global.argtypes = [
             P, ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int64,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P]
@@ -138,10 +142,12 @@ def dequant_row(desc: OrcDesc, kv: np.ndarray, page: int, off: int) -> np.ndarra
 
 def sparse_decode(*, q, kv, topk_idx, topk, swa, block_size, num_blocks, page_stride,
                   sm_scale, block_table=None, max_blocks_per_seq=None, valid_len=None,
-                  sink=None, num_splits=0, nthreads=None, scrub=False, s_q=1):
+                  sink=None, num_splits=0, nthreads=None, scrub=False, s_q=1, swa_pool=None):
     """Returns (out [B,H,512] f64, lse [B,H] f64, number of valid entries).
     scrub: read every non-finite dequantised cache element as 0.  s_q: query
-    tokens per sequence (block_table and valid_len have B / s_q rows)."""
+    tokens per sequence (block_table and valid_len have B / s_q rows).
+    swa_pool: dict(kv, block_table, block_size, num_blocks, page_stride,
+    max_blocks_per_seq) of a second pool the SWA entries resolve in."""
     q = _c(q, np.uint16)
     B, H, D = q.shape
     assert D == 512
@@ -157,9 +163,22 @@ def sparse_decode(*, q, kv, topk_idx, topk, swa, block_size, num_blocks, page_st
                      s_q=s_q)
     out = np.zeros((B, H, 512), dtype=np.float64)
     lse = np.zeros((B, H), dtype=np.float64)
-    n = lib().orc_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(bt), _ptr(ti),
-                                _ptr(vl), _ptr(sk), int(num_splits), _ptr(out), _ptr(lse),
-                                int(nthreads or default_threads()))
+    if swa_pool is None:
+        n = lib().orc_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(bt), _ptr(ti),
+                                    _ptr(vl), _ptr(sk), int(num_splits), _ptr(out), _ptr(lse),
+                                    int(nthreads or default_threads()))
+    else:
+        kv2 = _c(swa_pool["kv"], np.uint8)
+        bt2 = _c(swa_pool["block_table"], np.int32)
+        d2 = make_desc(B=B, H=H, topk=topk, swa=swa, block_size=swa_pool["block_size"],
+                       num_blocks=swa_pool["num_blocks"], page_stride=swa_pool["page_stride"],
+                       sm_scale=sm_scale, block_table=bt2,
+                       max_blocks_per_seq=swa_pool.get("max_blocks_per_seq"), scrub=scrub,
+                       s_q=s_q)
+        n = lib().orc_sparse_decode_dual(ctypes.byref(desc), ctypes.byref(d2), _ptr(q), _ptr(kv),
+                                         _ptr(bt), _ptr(kv2), _ptr(bt2), _ptr(ti), _ptr(vl),
+                                         _ptr(sk), int(num_splits), _ptr(out), _ptr(lse),
+                                         int(nthreads or default_threads()))
     return out, lse, int(n)
 
 
@@ -171,7 +190,8 @@ def decode_workload(w, *, topk_idx=None, use_block_table=True, num_splits=0, nth
               page_stride=w.page_stride, sm_scale=w.sm_scale,
               block_table=w.block_table if use_block_table else None,
               max_blocks_per_seq=w.max_blocks_per_seq if use_block_table else None,
-              valid_len=w.valid_len, sink=w.sink, s_q=getattr(w, "s_q", 1))
+              valid_len=w.valid_len, sink=w.sink, s_q=getattr(w, "s_q", 1),
+              swa_pool=getattr(w, "swa_pool", None))
     kw.update(overrides)
     return sparse_decode(num_splits=num_splits, nthreads=nthreads, **kw)
 

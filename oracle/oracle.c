@@ -148,6 +148,9 @@ typedef struct {
     const uint16_t* q;
     const uint8_t* kv;
     const int32_t* bt;
+    const orc_desc* d_swa;            /* second pool of the SWA entries, or NULL */
+    const uint8_t* kv_swa;
+    const int32_t* bt_swa;
     const int32_t* idx;
     const int32_t* valid_len;
     const float* sink;
@@ -289,10 +292,16 @@ static void* orc_worker(void* arg) {
             for (p = 0; p < eff_len; ++p) {
                 int32_t col = eff_to_col(d, vl, p);
                 int32_t idx = J->idx[(int64_t)b * Kt + col];
+                /* With a second pool, SWA entries (columns >= topk) name its
+                 * rows through its own block table and geometry. */
+                const int use_swa = J->d_swa != NULL && col >= d->topk;
+                const orc_desc* dp = use_swa ? J->d_swa : d;
+                const uint8_t* kvp = use_swa ? J->kv_swa : J->kv;
+                const int32_t* btp = use_swa ? J->bt_swa : J->bt;
                 int64_t page;
                 int32_t off;
-                valid[p] = (unsigned char)orc_resolve(d, J->bt, seq, idx, &page, &off);
-                if (valid[p]) orc_dequant_row(d, J->kv, page, off, rows + (int64_t)p * ORC_D);
+                valid[p] = (unsigned char)orc_resolve(dp, btp, seq, idx, &page, &off);
+                if (valid[p]) orc_dequant_row(dp, kvp, page, off, rows + (int64_t)p * ORC_D);
             }
             if (h == 0)
                 for (p = 0; p < eff_len; ++p) J->n_valid += valid[p];
@@ -307,6 +316,21 @@ int64_t orc_sparse_decode(const orc_desc* d, const uint16_t* q, const uint8_t* k
                           const int32_t* block_table, const int32_t* topk_idx,
                           const int32_t* valid_len, const float* sink, int32_t num_splits,
                           double* out, double* lse, int32_t nthreads) {
+    return orc_sparse_decode_dual(d, NULL, q, kv, block_table, NULL, NULL, topk_idx, valid_len,
+                                  sink, num_splits, out, lse, nthreads);
+}
+
+/* Dual-pool decode: the SWA entries resolve in a second fp8_ds_mla pool
+ * with its own block table, block size and page stride (DeepSeek-V4 keeps
+ * the sliding-window cache apart from the compressed "extra" cache the main
+ * top-k entries index: [vLLM-52212] implementation item 1, main/SWA work,
+ * and item 3, the extra cache).  d_swa NULL: one pool. */
+int64_t orc_sparse_decode_dual(const orc_desc* d, const orc_desc* d_swa, const uint16_t* q,
+                               const uint8_t* kv, const int32_t* block_table,
+                               const uint8_t* kv_swa, const int32_t* bt_swa,
+                               const int32_t* topk_idx, const int32_t* valid_len,
+                               const float* sink, int32_t num_splits, double* out, double* lse,
+                               int32_t nthreads) {
     int64_t items = (int64_t)d->B * d->H, total = 0;
     int32_t t, nt = nthreads < 1 ? 1 : nthreads;
     orc_job* jobs;
@@ -318,6 +342,7 @@ int64_t orc_sparse_decode(const orc_desc* d, const uint16_t* q, const uint8_t* k
     for (t = 0; t < nt; ++t) {
         orc_job* J = &jobs[t];
         J->d = d; J->q = q; J->kv = kv; J->bt = block_table; J->idx = topk_idx;
+        J->d_swa = d_swa; J->kv_swa = kv_swa; J->bt_swa = bt_swa;
         J->valid_len = valid_len; J->sink = sink; J->num_splits = num_splits;
         J->out = out; J->lse = lse;
         J->item_begin = items * t / nt;

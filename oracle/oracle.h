@@ -62,6 +62,16 @@ int64_t orc_sparse_decode(const orc_desc* d, const uint16_t* q, const uint8_t* k
                           const int32_t* valid_len, const float* sink, int32_t num_splits,
                           double* out, double* lse, int32_t nthreads);
 
+/* Dual-pool decode: entries at columns >= topk (the SWA part) resolve and
+ * dequantise in the second pool (d_swa geometry, kv_swa, bt_swa); d_swa
+ * NULL means one pool.  Other arguments as orc_sparse_decode. */
+int64_t orc_sparse_decode_dual(const orc_desc* d, const orc_desc* d_swa, const uint16_t* q,
+                               const uint8_t* kv, const int32_t* block_table,
+                               const uint8_t* kv_swa, const int32_t* bt_swa,
+                               const int32_t* topk_idx, const int32_t* valid_len,
+                               const float* sink, int32_t num_splits, double* out, double* lse,
+                               int32_t nthreads);
+
 /* Req-local -> global slot conversion.  Dense when cu_seqlens is NULL
  * (out[t*width + i]); ragged otherwise (out[cu[t] + i], i < cu[t+1]-cu[t]).
  * req_id may be NULL (request t for token t). */

@@ -19,5 +19,6 @@ from .workloads import (  # noqa: F401
     make_custom,
     make_writer_rows,
     poison_rows,
+    split_swa_pool,
     workload_digest,
 )

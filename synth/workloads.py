@@ -84,6 +84,9 @@ class Workload:
     # rounding [n,448] as float32, RoPE values before bf16 rounding [n,64]).
     source_rows: Optional[tuple] = None
     s_q: int = 1                  # query tokens per sequence: B = sequences * s_q
+    # A second pool for the SWA entries (dict: kv, block_table, block_size,
+    # num_blocks, page_stride, max_blocks_per_seq), or None: one pool.
+    swa_pool: Optional[dict] = None
 
     @property
     def Kt(self) -> int:
@@ -356,3 +359,59 @@ def make_writer_rows(n: int, seed: int, *, specials: bool = True, spread: int = 
             if i % 16 == 0:
                 bits[i, 448 + int(rng.integers(0, 64))] = [0x7FC0, 0x7F80, 0xFF80][int(rng.integers(0, 3))]
     return bits
+
+
+
+def split_swa_pool(w: Workload, *, block_size: int, seed: int, page_pad: int = 0,
+                   slack_frac: float = 0.02) -> Workload:
+    """Moves the rows that SWA entries (index columns >= topk) name into a
+    second fp8_ds_mla pool with its own shuffled pages, block table and block
+    size; rows that only SWA entries name become 0xFF poison in the first
+    pool, so reading an SWA row from the wrong pool cannot go unnoticed.
+    Index lists, q and lengths are unchanged (SWA indices stay req-local
+    slots, now resolved through the second block table)."""
+    rng = np.random.default_rng(seed)
+    bs2 = int(block_size)
+    B = w.block_table.shape[0]
+    seq_lens = np.asarray(w.seq_lens, dtype=np.int64)
+    pages_per_seq = (seq_lens + bs2 - 1) // bs2
+    needed = int(pages_per_seq.sum())
+    pool = needed + int(math.ceil(slack_frac * needed))
+    perm = rng.permutation(pool).astype(np.int64)
+    max_blocks = max(int(pages_per_seq.max()), 1)
+    bt2 = np.full((B, max_blocks), -1, dtype=np.int32)
+    cursor = 0
+    for b in range(B):
+        n = int(pages_per_seq[b])
+        bt2[b, :n] = perm[cursor:cursor + n]
+        cursor += n
+    stride2 = bs2 * ROW_BYTES + int(page_pad)
+    kv2 = np.full((pool, stride2), POISON, dtype=np.uint8)
+    kv1 = w.kv.copy()
+    bs1 = w.block_size
+
+    def addr(kv_stride, pg, off, bs):
+        return pg * kv_stride + off * ROW_DATA_BYTES, pg * kv_stride + bs * ROW_DATA_BYTES + off * ROW_SCALE_BYTES
+
+    main_used, swa_used = set(), set()
+    for t in range(w.B):
+        r = t // w.s_q
+        for k, idx in enumerate(w.topk_idx[t]):
+            if idx < 0:
+                continue
+            (swa_used if k >= w.topk else main_used).add((r, int(idx)))
+    f1, f2 = w.kv.reshape(-1), kv2.reshape(-1)
+    k1 = kv1.reshape(-1)
+    for r, slot in sorted(swa_used):
+        p1 = int(w.block_table[r, slot // bs1])
+        d1, s1 = addr(w.page_stride, p1, slot % bs1, bs1)
+        p2 = int(bt2[r, slot // bs2])
+        d2, s2 = addr(stride2, p2, slot % bs2, bs2)
+        f2[d2:d2 + ROW_DATA_BYTES] = f1[d1:d1 + ROW_DATA_BYTES]
+        f2[s2:s2 + ROW_SCALE_BYTES] = f1[s1:s1 + ROW_SCALE_BYTES]
+        if (r, slot) not in main_used:
+            k1[d1:d1 + ROW_DATA_BYTES] = POISON
+            k1[s1:s1 + ROW_SCALE_BYTES] = POISON
+    return dataclasses.replace(w, kv=kv1, swa_pool=dict(
+        kv=kv2, block_table=bt2, block_size=bs2, num_blocks=pool, page_stride=stride2,
+        max_blocks_per_seq=max_blocks))

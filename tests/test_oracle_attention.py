@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from synth import make_custom, poison_rows
+from synth import make_custom, poison_rows, split_swa_pool
 
 RTOL = 1e-10
 ATOL = 1e-12
@@ -313,3 +313,22 @@ def test_multi_token_equals_single_token_with_expanded_tables():
     vl = np.repeat(w.valid_len, 4)
     o1, l1, n1 = oracle.decode_workload(w, block_table=bt, valid_len=vl, s_q=1)
     assert n == n1 and np.array_equal(out, o1) and np.array_equal(lse, l1)
+
+
+@pytest.mark.parametrize("bs2", [16, 1, 64])
+def test_dual_pool_decode_matches_sdpa(bs2):
+    """SWA entries resolved through a second pool (own pages, block table and
+    block size; the first pool holds poison where only SWA rows were)."""
+    w = split_swa_pool(_w(130 + bs2), block_size=bs2, seed=131)
+    out, lse, _ = oracle.decode_workload(w)
+    ro, rl = sdpa_reference(w)
+    np.testing.assert_allclose(out, ro, rtol=RTOL, atol=ATOL)
+    np.testing.assert_allclose(lse, rl, rtol=RTOL, atol=ATOL)
+
+
+def test_dual_pool_equals_the_single_pool_it_was_split_from():
+    w = _w(140, s_q=2)
+    w2 = split_swa_pool(w, block_size=16, seed=141, page_pad=24)
+    a = oracle.decode_workload(w, num_splits=3)
+    b = oracle.decode_workload(w2, num_splits=3)
+    assert a[2] == b[2] and np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -70,6 +70,10 @@ MUTANTS = {
                     "const int32_t seq = b;"),
     "s_q_table_only": ("valid[p] = (unsigned char)orc_resolve(d, J->bt, seq, idx, &page, &off);",
                        "valid[p] = (unsigned char)orc_resolve(d, J->bt, b, idx, &page, &off);"),
+    "swa_pool_ignored": ("const int use_swa = J->d_swa != NULL && col >= d->topk;",
+                         "const int use_swa = 0;"),
+    "swa_pool_for_all": ("const int use_swa = J->d_swa != NULL && col >= d->topk;",
+                         "const int use_swa = J->d_swa != NULL;"),
     "dot_skips_rope": ("for (j = 0; j < ORC_D; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];",
                        "for (j = 0; j < 448; ++j) dot += qd[j] * rows[(int64_t)p * ORC_D + j];"),
 }
@@ -122,7 +126,7 @@ real = oracle.lib()
 mut = ctypes.CDLL(sys.argv[1])
 for n in ("orc_e4m3fn", "orc_ue8m0", "orc_bf16", "orc_resolve", "orc_dequant_row",
           "orc_sparse_decode", "orc_convert_req_index_to_global", "orc_quantize_row",
-          "orc_store_rows"):
+          "orc_store_rows", "orc_sparse_decode_dual"):
     f, g = getattr(mut, n), getattr(real, n)
     f.argtypes, f.restype = g.argtypes, g.restype
 oracle._lib = mut
