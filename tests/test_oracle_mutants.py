@@ -68,8 +68,8 @@ MUTANTS = {
                             "data[ORC_DNOPE + 2 * r] = (uint8_t)(bits >> 8);"),
     "s_q_ignored": ("const int32_t seq = d->s_q > 1 ? b / d->s_q : b;",
                     "const int32_t seq = b;"),
-    "s_q_table_only": ("valid[p] = (unsigned char)orc_resolve(d, J->bt, seq, idx, &page, &off);",
-                       "valid[p] = (unsigned char)orc_resolve(d, J->bt, b, idx, &page, &off);"),
+    "s_q_table_only": ("valid[p] = (unsigned char)orc_resolve(dp, btp, seq, idx, &page, &off);",
+                       "valid[p] = (unsigned char)orc_resolve(dp, btp, b, idx, &page, &off);"),
     "swa_pool_ignored": ("const int use_swa = J->d_swa != NULL && col >= d->topk;",
                          "const int use_swa = 0;"),
     "swa_pool_for_all": ("const int use_swa = J->d_swa != NULL && col >= d->topk;",
