@@ -228,6 +228,33 @@ int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
                         const void* part_out, const float* part_lse, const float* sink,
                         void* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------- dual cache */
+
+/* One fp8_ds_mla pool: its pages and how a sequence's req-local slots map
+ * onto them (geometry as in dsv4_decode_desc). */
+typedef struct dsv4_cache_pool {
+    const void* kv_cache;          /* uint8 [num_blocks, page_stride], 8-byte aligned */
+    const int32_t* block_table;    /* int32 [B / s_q, block_table_stride] or NULL     */
+    int64_t num_blocks;            /* >= 1                                            */
+    int64_t page_stride;           /* multiple of 8, >= block_size * 584              */
+    int64_t block_table_stride;    /* elements between block-table rows               */
+    int32_t block_size;            /* slots per page, >= 1                            */
+    int32_t max_blocks_per_seq;    /* usable block-table columns                      */
+} dsv4_cache_pool;
+
+/* Dual-cache decode: as dsv4_sparse_decode, except that main entries
+ * (columns [0, topk)) resolve in main_pool and sliding-window entries
+ * (columns [topk, topk+swa)) in swa_pool, each through its own block table,
+ * block size and page stride.  The cache geometry fields of desc are
+ * ignored (the pools carry it); both pools have a block table or neither
+ * does.  (vLLM PR #52212 page: main/SWA work in one kernel, implementation
+ * item 1, next to a separate compressed "extra" cache, item 3; DeepSeek-V4
+ * keeps its sliding-window cache apart from that cache.) */
+int dsv4_sparse_decode_dual(const dsv4_decode_desc* desc, const void* q,
+                            const dsv4_cache_pool* main_pool, const dsv4_cache_pool* swa_pool,
+                            const int32_t* topk_idx, const int32_t* valid_len, const float* sink,
+                            void* out, float* lse, int32_t num_splits, hipStream_t stream);
+
 /* -------------------------------------------------- two-kernel path */
 
 /* The two-kernel decode: gather + dequantise into a dense bf16 buffer, then

@@ -55,6 +55,31 @@ class dsv4_decode_desc(ctypes.Structure):
     ]
 
 
+class dsv4_cache_pool(ctypes.Structure):
+    _fields_ = [
+        ("kv_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("page_stride", ctypes.c_int64),
+        ("block_table_stride", ctypes.c_int64),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+    ]
+
+
+def make_pool(kv_cache: torch.Tensor, block_table: Optional[torch.Tensor], *, block_size: int,
+              max_blocks_per_seq: int = 0) -> dsv4_cache_pool:
+    """A pool over a [num_blocks, page_stride] uint8 cache tensor."""
+    pl = dsv4_cache_pool()
+    pl.kv_cache = kv_cache.data_ptr()
+    pl.block_table = block_table.data_ptr() if block_table is not None else None
+    pl.num_blocks, pl.page_stride = kv_cache.shape[0], kv_cache.shape[1]
+    pl.block_table_stride = block_table.shape[1] if block_table is not None else 0
+    pl.block_size = block_size
+    pl.max_blocks_per_seq = max_blocks_per_seq
+    return pl
+
+
 class dsv4_plan(ctypes.Structure):
     _fields_ = [
         ("num_splits", ctypes.c_int32),
@@ -98,6 +123,10 @@ _lib.dsv4_gather_floor.argtypes = [_DESC, _P, _P, _P, _P, ctypes.c_int32, _P, _P
 _lib.dsv4_gather_floor.restype = ctypes.c_int
 _lib.dsv4_decode_flags_for_cache.argtypes = [ctypes.c_int32] * 4
 _lib.dsv4_decode_flags_for_cache.restype = ctypes.c_uint32
+_lib.dsv4_sparse_decode_dual.argtypes = [_DESC, _P, ctypes.POINTER(dsv4_cache_pool),
+                                         ctypes.POINTER(dsv4_cache_pool), _P, _P, _P, _P, _P,
+                                         ctypes.c_int32, _P]
+_lib.dsv4_sparse_decode_dual.restype = ctypes.c_int
 _lib.dsv4_gather_dequant.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P]
 _lib.dsv4_gather_dequant.restype = ctypes.c_int
 _lib.dsv4_dense_decode.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]
@@ -213,6 +242,17 @@ def dsv4_decode_flags_for_cache(*, cache_is_fp8_ds_mla: bool, has_kv_transfer: b
                                 has_extra_cache: bool, writer_sanitizes: bool) -> int:
     return int(_lib.dsv4_decode_flags_for_cache(int(cache_is_fp8_ds_mla), int(has_kv_transfer),
                                                 int(has_extra_cache), int(writer_sanitizes)))
+
+
+def dsv4_sparse_decode_dual(desc, q: torch.Tensor, main_pool: dsv4_cache_pool,
+                            swa_pool: dsv4_cache_pool, topk_idx: torch.Tensor,
+                            valid_len: Optional[torch.Tensor], sink: Optional[torch.Tensor],
+                            out: torch.Tensor, lse: Optional[torch.Tensor], num_splits: int = 0,
+                            stream=None) -> None:
+    _check(_lib.dsv4_sparse_decode_dual(ctypes.byref(desc), _ptr(q), ctypes.byref(main_pool),
+                                        ctypes.byref(swa_pool), _ptr(topk_idx), _ptr(valid_len),
+                                        _ptr(sink), _ptr(out), _ptr(lse), num_splits,
+                                        _stream(stream)))
 
 
 def dsv4_gather_dequant(desc, kv_cache: torch.Tensor, block_table: Optional[torch.Tensor],

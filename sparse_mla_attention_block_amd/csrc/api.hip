@@ -173,6 +173,11 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.idx = idx;
     p.valid_len = valid_len;
     p.mask = nullptr;
+    p.kv2 = nullptr;
+    p.bt2 = nullptr;
+    p.num_blocks2 = p.bt_stride2 = p.page_stride2 = 0;
+    p.bs2 = 1;
+    p.max_blocks2 = 0;
     p.sink = sink;
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
@@ -205,16 +210,45 @@ int launched(hipError_t e, const char* what) {
     return ok();
 }
 
+int check_pool(const dsv4_cache_pool* pl, const char* which) {
+    if (!pl || !pl->kv_cache)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "%s pool: kv_cache must not be NULL", which);
+    if (!aligned(pl->kv_cache, 8))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "%s pool: kv_cache must be 8-byte aligned", which);
+    if (pl->block_size < 1 || pl->num_blocks < 1)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "%s pool: block_size and num_blocks must be >= 1",
+                    which);
+    if (pl->page_stride < (int64_t)pl->block_size * dsv4::kRowBytes || pl->page_stride % 8)
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "%s pool: page_stride must be a multiple of 8 and >= block_size*584", which);
+    if (pl->num_blocks > INT64_MAX / pl->page_stride)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "%s pool: num_blocks * page_stride overflows", which);
+    if (pl->block_table &&
+        (pl->max_blocks_per_seq < 1 || pl->block_table_stride < pl->max_blocks_per_seq))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "%s pool: bad block-table geometry", which);
+    return DSV4_OK;
+}
+
 int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const int32_t* bt,
                 const int32_t* idx, const int32_t* valid_len, const float* sink, void* out,
-                float* lse, int32_t num_splits, hipStream_t stream, bool with_combine) {
+                float* lse, int32_t num_splits, hipStream_t stream, bool with_combine,
+                const dsv4_cache_pool* swa_pool = nullptr) {
     Shape sh;
     dsv4_plan plan;
     int st = make_plan(d, num_splits, &sh, &plan);
     if (st) return st;
     st = check_decode_ptrs(d, plan, q, kv, bt, idx, out);
     if (st) return st;
-    const dsv4::DecodeParams p = make_params(d, sh, q, kv, bt, idx, valid_len, sink, out, lse);
+    dsv4::DecodeParams p = make_params(d, sh, q, kv, bt, idx, valid_len, sink, out, lse);
+    if (swa_pool) {
+        p.kv2 = static_cast<const uint8_t*>(swa_pool->kv_cache);
+        p.bt2 = swa_pool->block_table;
+        p.num_blocks2 = swa_pool->num_blocks;
+        p.bt_stride2 = swa_pool->block_table_stride;
+        p.page_stride2 = swa_pool->page_stride;
+        p.bs2 = swa_pool->block_size;
+        p.max_blocks2 = swa_pool->block_table ? swa_pool->max_blocks_per_seq : 0;
+    }
     (void)hipGetLastError();   // start from a clean error state
     st = launched(dsv4::launch_decode_partial(p, sh.hg, plan.grid_partial,
                                                           (d->flags & DSV4_DECODE_SCRUB) != 0,
@@ -440,6 +474,28 @@ int dsv4_dense_decode(const dsv4_decode_desc* desc, const void* q, const void* k
     c.H = desc->num_heads;
     c.S = sh.splits;
     return launched(dsv4::launch_combine(c, stream), "combine");
+}
+
+int dsv4_sparse_decode_dual(const dsv4_decode_desc* desc, const void* q,
+                            const dsv4_cache_pool* main_pool, const dsv4_cache_pool* swa_pool,
+                            const int32_t* topk_idx, const int32_t* valid_len, const float* sink,
+                            void* out, float* lse, int32_t num_splits, hipStream_t stream) {
+    if (!desc) return fail(DSV4_ERR_INVALID_ARGUMENT, "desc must not be NULL");
+    int st = check_pool(main_pool, "main");
+    if (st) return st;
+    st = check_pool(swa_pool, "swa");
+    if (st) return st;
+    if ((main_pool->block_table == nullptr) != (swa_pool->block_table == nullptr))
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "both pools need a block table, or neither (global slots)");
+    dsv4_decode_desc d = *desc;
+    d.block_size = main_pool->block_size;
+    d.num_blocks = main_pool->num_blocks;
+    d.page_stride = main_pool->page_stride;
+    d.block_table_stride = main_pool->block_table_stride;
+    d.max_blocks_per_seq = main_pool->max_blocks_per_seq;
+    return decode_impl(&d, q, main_pool->kv_cache, main_pool->block_table, topk_idx, valid_len,
+                       sink, out, lse, num_splits, stream, true, swa_pool);
 }
 
 int dsv4_quantize_store(const void* rows, int64_t row_stride, const int64_t* slot_mapping,

@@ -263,26 +263,48 @@ __device__ __forceinline__ int32_t load_index(const DecodeParams& p, int b, int 
     return in ? v : -1;
 }
 
-__device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, int seq, int32_t idx) {
+// The pool an entry resolves in: the second (SWA) pool of a dual cache for
+// entries of the SWA part (effective position >= vl), else the first.  Both
+// pools have a block table or neither does, so the table test stays uniform.
+struct Pool {
+    const uint8_t* kv;
+    const int32_t* bt;
+    int64_t num_blocks, bt_stride, page_stride;
+    int32_t bs, max_blocks;
+};
+
+__device__ __forceinline__ Pool pool_of(const DecodeParams& p, bool swa_entry) {
+    const bool u = swa_entry && p.kv2 != nullptr;
+    return Pool{u ? p.kv2 : p.kv,
+                u ? p.bt2 : p.bt,
+                u ? p.num_blocks2 : p.num_blocks,
+                u ? p.bt_stride2 : p.bt_stride,
+                u ? p.page_stride2 : p.page_stride,
+                u ? p.bs2 : p.bs,
+                u ? p.max_blocks2 : p.max_blocks};
+}
+
+__device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, const Pool& pl, int seq,
+                                               int32_t idx) {
     const bool ok = idx >= 0;
-    const int64_t blk = (ok ? idx : 0) / p.bs;
+    const int64_t blk = (ok ? idx : 0) / pl.bs;
     if (p.bt) {
-        const bool inb = ok && blk < p.max_blocks;
-        const int32_t pg = p.bt[(int64_t)seq * p.bt_stride + (inb ? blk : 0)];
-        return (inb && pg >= 0 && pg < p.num_blocks) ? pg : -1;
+        const bool inb = ok && blk < pl.max_blocks;
+        const int32_t pg = pl.bt[(int64_t)seq * pl.bt_stride + (inb ? blk : 0)];
+        return (inb && pg >= 0 && pg < pl.num_blocks) ? pg : -1;
     }
-    return (ok && blk < p.num_blocks) ? blk : -1;
+    return (ok && blk < pl.num_blocks) ? blk : -1;
 }
 
 // Data and scale-word addresses of the row at (page, idx % bs); the zero row
 // for a row that takes no part.
-__device__ __forceinline__ void write_meta(const DecodeParams& p, int64_t* row, int64_t page,
+__device__ __forceinline__ void write_meta(const Pool& pl, int64_t* row, int64_t page,
                                            int32_t idx) {
-    const int64_t off = idx % p.bs;
-    const uint8_t* pg = p.kv + page * p.page_stride;
+    const int64_t off = idx % pl.bs;
+    const uint8_t* pg = pl.kv + page * pl.page_stride;
     row[0] = reinterpret_cast<int64_t>(page >= 0 ? pg + off * kRowData : kZeroRow);
     row[1] = reinterpret_cast<int64_t>(
-        page >= 0 ? pg + (int64_t)p.bs * kRowData + off * kRowScale : kZeroRow + kRowData);
+        page >= 0 ? pg + (int64_t)pl.bs * kRowData + off * kRowScale : kZeroRow + kRowData);
 }
 
 // Reductions across the four 16-lane rows of a wave.  v_permlane16_swap
@@ -397,10 +419,12 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         } else {
             const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
             const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
-            const int64_t g0 = lookup_page(p, seq, i0);
-            const int64_t g1 = lookup_page(p, seq, i1);
-            write_meta(p, meta + 2 * tid, g0, i0);
-            write_meta(p, meta + 2 * (kThreads + tid), g1, i1);
+            const Pool pl0 = pool_of(p, lo + tid >= vl);
+            const Pool pl1 = pool_of(p, lo + kThreads + tid >= vl);
+            const int64_t g0 = lookup_page(p, pl0, seq, i0);
+            const int64_t g1 = lookup_page(p, pl1, seq, i1);
+            write_meta(pl0, meta + 2 * tid, g0, i0);
+            write_meta(pl1, meta + 2 * (kThreads + tid), g1, i1);
             b0 = __builtin_amdgcn_ballot_w64(g0 >= 0);
             b1 = __builtin_amdgcn_ballot_w64(g1 >= 0);
         }
@@ -455,15 +479,15 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         const int col = cpos < vl ? cpos : p.topk + (cpos - vl);
         return p.idx[(int64_t)b * p.idx_stride + (pos < hi ? col : 0)];
     };
-    auto bt_col = [&](int32_t idx) {
-        const int64_t blk = idx / p.bs;
-        return idx >= 0 && blk < p.max_blocks ? blk : (int64_t)0;
+    auto bt_col = [&](const Pool& pl, int32_t idx) {
+        const int64_t blk = idx / pl.bs;
+        return idx >= 0 && blk < pl.max_blocks ? blk : (int64_t)0;
     };
-    auto page_of = [&](int32_t idx, int32_t raw) -> int64_t {
+    auto page_of = [&](const Pool& pl, int32_t idx, int32_t raw) -> int64_t {
         if (idx < 0) return -1;
-        const int64_t blk = idx / p.bs;
-        if (p.bt) return blk < p.max_blocks && raw >= 0 && raw < p.num_blocks ? raw : -1;
-        return blk < p.num_blocks ? blk : -1;
+        const int64_t blk = idx / pl.bs;
+        if (p.bt) return blk < pl.max_blocks && raw >= 0 && raw < pl.num_blocks ? raw : -1;
+        return blk < pl.num_blocks ? blk : -1;
     };
     auto resolve_stage = [&](int t) __attribute__((always_inline)) {
         const int ph = t % kHalfTiles;
@@ -498,14 +522,16 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             r_i0 = e0 < hi ? r_i0 : -1;
             r_i1 = e0 + 64 < hi ? r_i1 : -1;
             if (p.bt) {
-                r_p0 = p.bt[(int64_t)seq * p.bt_stride + bt_col(r_i0)];
-                r_p1 = p.bt[(int64_t)seq * p.bt_stride + bt_col(r_i1)];
+                const Pool pl0 = pool_of(p, e0 >= vl), pl1 = pool_of(p, e0 + 64 >= vl);
+                r_p0 = pl0.bt[(int64_t)seq * pl0.bt_stride + bt_col(pl0, r_i0)];
+                r_p1 = pl1.bt[(int64_t)seq * pl1.bt_stride + bt_col(pl1, r_i1)];
             }
         } else {
-            const int64_t pg0 = page_of(r_i0, r_p0), pg1 = page_of(r_i1, r_p1);
+            const Pool pl0 = pool_of(p, e0 >= vl), pl1 = pool_of(p, e0 + 64 >= vl);
+            const int64_t pg0 = page_of(pl0, r_i0, r_p0), pg1 = page_of(pl1, r_i1, r_p1);
             int64_t* m = meta_tile(nxt) + 2 * (128 * wave + lane);
-            write_meta(p, m, pg0, r_i0);
-            write_meta(p, m + 2 * 64, pg1, r_i1);
+            write_meta(pl0, m, pg0, r_i0);
+            write_meta(pl1, m + 2 * 64, pg1, r_i1);
             const uint64_t b0 = __builtin_amdgcn_ballot_w64(pg0 >= 0);
             const uint64_t b1 = __builtin_amdgcn_ballot_w64(pg1 >= 0);
             if (lane == 0) {
@@ -825,9 +851,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(const De
     const int vl = p.valid_len ? min(max(p.valid_len[seq], 0), p.topk) : p.topk;
     const int32_t raw = p.idx[(int64_t)b * p.idx_stride + col];
     const int32_t idx = col < p.topk && col >= vl ? -1 : raw;
-    const int64_t page = lookup_page(p, seq, idx);
+    const Pool pl = pool_of(p, col >= p.topk);
+    const int64_t page = lookup_page(p, pl, seq, idx);
     int64_t m[2];
-    write_meta(p, m, page, idx);
+    write_meta(pl, m, page, idx);
     uint32_t rr[64];
     load_patch<0>(PatchSrc{(gbyte*)m[0], (gbyte*)m[1]}, l8, rr);
     uint16_t* dst = kv_out + ((int64_t)b * Kt + col) * kD;
@@ -939,12 +966,9 @@ __global__ __launch_bounds__(kThreads) void gather_floor_kernel(const DecodePara
         for (int e = 0; e < 2; ++e) {
             const int i = tid + e * kThreads;
             const int32_t id = load_index(p, b, vl, hi, base + i);
-            const int64_t pg = lookup_page(p, seq, id);
-            const uint8_t* pgp = p.kv + pg * p.page_stride;
-            const int64_t off = id % p.bs;
-            addr[i][0] = reinterpret_cast<int64_t>(pg >= 0 ? pgp + off * kRowData : kZeroRow);
-            addr[i][1] = reinterpret_cast<int64_t>(
-                pg >= 0 ? pgp + (int64_t)p.bs * kRowData + off * kRowScale : kZeroRow + kRowData);
+            const Pool pl = pool_of(p, base + i >= vl);
+            const int64_t pg = lookup_page(p, pl, seq, id);
+            write_meta(pl, addr[i], pg, id);
         }
         __syncthreads();
         const int n = min(hi - base, kRing);

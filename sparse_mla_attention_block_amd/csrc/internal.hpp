@@ -68,6 +68,11 @@ struct DecodeParams {
     const int32_t* idx;         // [B, idx_stride]
     const int32_t* valid_len;   // [B / sq] or null
     const uint8_t* mask;        // dense source only: [B, idx_stride], 1 = no part
+    // Dual cache: the pool SWA entries resolve in (kv2 null: one pool).
+    const uint8_t* kv2;
+    const int32_t* bt2;
+    int64_t num_blocks2, bt_stride2, page_stride2;
+    int32_t bs2, max_blocks2;
     const float* sink;          // [H] or null
     uint16_t* out;              // bf16 [B, H, 512] (direct output, S == 1)
     float* lse;                 // [B, H] or null (direct output, S == 1)

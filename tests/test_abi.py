@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
                  "dsv4_convert_req_index_to_global", "dsv4_sparse_decode_plan",
                  "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error",
                  "dsv4_gather_floor", "dsv4_quantize_store", "dsv4_gather_dequant",
-                 "dsv4_dense_decode", "dsv4_decode_flags_for_cache"):
+                 "dsv4_dense_decode", "dsv4_decode_flags_for_cache", "dsv4_sparse_decode_dual"):
         assert want in names
 
 
@@ -48,7 +48,7 @@ def test_library_is_built_for_gfx950_only():
         assert other not in data
 
 
-@pytest.mark.parametrize("struct", ["dsv4_decode_desc", "dsv4_plan"])
+@pytest.mark.parametrize("struct", ["dsv4_decode_desc", "dsv4_plan", "dsv4_cache_pool"])
 def test_binding_structs_match_the_c_layout(struct, tmp_path):
     """Every field of the Python mirror sits at the offset a C compiler gives
     it in include/dsv4.h, and the sizes agree."""
@@ -257,3 +257,27 @@ def test_provenance_gate_truth_table():
                                                  has_extra_cache=extra, writer_sanitizes=san)
         trusted = fmt and not xfer and extra and san
         assert flags == (0 if trusted else dsv4.DSV4_DECODE_SCRUB), (fmt, xfer, extra, san)
+
+
+def test_dual_cache_validation_without_touching_the_gpu():
+    lib = dsv4._lib
+    fake = ctypes.c_void_p(4096)
+    E = dsv4.DSV4_ERR_INVALID_ARGUMENT
+    d = _desc(2, 64, 100, 20)
+
+    def pool(bt=fake, bs=64, nb=10, stride=64 * 584, kv=fake):
+        pl = dsv4.dsv4_cache_pool()
+        pl.kv_cache, pl.block_table = kv, bt
+        pl.num_blocks, pl.page_stride, pl.block_table_stride = nb, stride, 16
+        pl.block_size, pl.max_blocks_per_seq = bs, 16
+        return pl
+
+    def call(a, b, q=fake):
+        return lib.dsv4_sparse_decode_dual(ctypes.byref(d), q, ctypes.byref(a), ctypes.byref(b),
+                                           fake, None, None, fake, None, 1, None)
+    assert call(pool(), pool(bt=None)) == E              # tables on one side only
+    assert call(pool(), pool(bs=0)) == E
+    assert call(pool(), pool(stride=16 * 584)) == E      # stride below block_size * 584
+    assert call(pool(kv=None), pool()) == E
+    assert call(pool(), pool(), q=None) == E
+    assert "swa pool" in (call(pool(), pool(nb=0)) == E and dsv4.dsv4_last_error())
