@@ -278,6 +278,54 @@ def main() -> int:
     torch.cuda.synchronize()
     same = bool(torch.equal(out_timed, out) and torch.equal(lse_timed, lse))
 
+    # B-sweep of the headline shape: B tokens per step with the same index
+    # list, token b of a step reading its own cache replica (same rows,
+    # different addresses), the replicas rotated across steps.
+    sweep = []
+    K2 = min(K, 400)
+    for Bs in (2, 4, 8, 16, 32, 64):
+        if 2 * Bs > R:
+            break
+        dk = dict(batch=Bs, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
+                  num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale)
+        plan_s = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**dk), 0)
+        Ss = plan_s.num_splits
+        ws_s = torch.empty(max(plan_s.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+        desc_s = dsv4.make_desc(workspace=ws_s, **dk)
+        po_s, pl_s = dsv4.workspace_split_views(ws_s, Bs, H, Ss) if Ss > 1 else (None, None)
+        q_s = q.expand(Bs, H, 512).contiguous()
+        idx_s = idx.expand(Bs, Kt).contiguous()
+        gs = torch.empty((Bs, Kt), dtype=torch.int32, device=dev)
+        out_s = torch.empty((Bs, H, 512), dtype=torch.bfloat16, device=dev)
+        lse_s = torch.empty((Bs, H), dtype=torch.float32, device=dev)
+        nrot = R // Bs
+
+        def step_s(r, Bs=Bs, Ss=Ss, desc_s=desc_s, po_s=po_s, pl_s=pl_s, q_s=q_s, idx_s=idx_s,
+                   gs=gs, out_s=out_s, lse_s=lse_s, nrot=nrot):
+            start = (r % nrot) * Bs
+            dsv4.dsv4_convert_req_index_to_global(None, Bs, bt_all[start:start + Bs], maxb, maxb,
+                                                  idx_s, Kt, Bs, Kt, w.block_size, None, -1, gs)
+            dsv4.dsv4_sparse_decode_partial(desc_s, q_s, kv, None, gs, None, sink, out_s, lse_s,
+                                            Ss)
+            if Ss > 1:
+                dsv4.dsv4_combine_splits(Bs, H, Ss, po_s, pl_s, sink, out_s, lse_s)
+
+        ms_s = time_graph(capture(step_s, K2), K2)
+        bytes_s = Bs * (n_valid_slots * (ROW_BYTES + INDEX_BYTES) + H * 512 * 2 * 2)
+        sweep.append({"B": Bs, "num_splits": Ss, "heads_per_group": plan_s.heads_per_group,
+                      "ms_per_step": ms_s, "tokens_per_s": Bs * n_valid_slots / (ms_s * 1e-3),
+                      "GBps": bytes_s / (ms_s * 1e-3) / 1e9,
+                      "frac": bytes_s / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBPS})
+        del ws_s, q_s, idx_s, gs, out_s, lse_s
+
+    # A measured bandwidth reference: a 1 GiB device-to-device copy.
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    csrc.fill_(1)
+    kt_copy = time_graph(capture(lambda r: cdst.copy_(csrc), 20), 20)
+    copy_GBps = 2 * (1 << 30) / (kt_copy * 1e-3) / 1e9
+    del csrc, cdst
+
     # Algorithmic work: valid entries (rows + index) and q per launch of the
     # partial kernel; flops 2*512*H per entry for QK and again for PV.
     n_valid = n_valid_slots
@@ -320,6 +368,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
+            "frac_of_measured_copy": achieved / copy_GBps,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": part_bytes,
             "mfma_frac": flops / (kt_part * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
@@ -327,6 +376,8 @@ def main() -> int:
         "kernels_ms": {"convert": kt_conv, "decode_partial": kt_part, "combine": kt_comb},
         "floors_ms": {"gather_only": kt_gather, "empty_launch": kt_empty,
                       "partial_over_gather": kt_part / kt_gather},
+        "measured_copy_GBps": copy_GBps,
+        "b_sweep": sweep,
         "event_ms_per_step": ev_ms_per_step,
         "writer": {"rows": wn, "block_size": wbs, "sanitize": True, "replicas": wrep,
                    "ms": kt_writer, "algorithmic_bytes": writer_bytes,
@@ -433,6 +484,16 @@ def two_kernel_leg(dev, capture_fn=None, K=50):
     }
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, out_gpu, lse_gpu, seconds):
     """The fp64 CPU oracle, as it stands, timed on this host over repeated
     full decodes of the same workload (about `seconds` of CPU work)."""
@@ -449,6 +510,15 @@ def cpu_baseline(w, out_gpu, lse_gpu, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    # The same oracle on one thread, over a third of the time budget.
+    reps1 = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.decode_workload(w, nthreads=1)
+        reps1 += 1
+        if time.perf_counter() - t1 >= seconds / 3:
+            break
+    dt1 = time.perf_counter() - t1
     got = out_gpu.float().double().cpu().numpy()
     err = np.abs(got - ref[0])
     bound = 2e-2 + 1e-2 * np.abs(ref[0])
@@ -461,6 +531,9 @@ def cpu_baseline(w, out_gpu, lse_gpu, seconds):
         "sample": f"{reps} full decodes of the benchmark workload ({n_valid} valid entries x "
                   f"64 heads each), fp64 C oracle, {threads} threads, {dt:.1f} s",
         "host_cpus": os.cpu_count(),
+        "cpu_model": _cpu_model(),
+        "single_thread": {"value": reps1 * n_valid / dt1, "cores": 1,
+                          "sample": f"{reps1} full decodes, 1 thread, {dt1:.1f} s"},
         "parity_vs_gpu": {"max_abs_out_err": float(err.max()),
                           "within_tolerance": bool((err <= bound).all()) and lse_err <= 1e-3,
                           "max_abs_lse_err": lse_err},

@@ -132,10 +132,13 @@ typedef struct dsv4_plan {
 
 /* Plan a decode without launching anything: validates the descriptor
  * (pointers other than workspace are not looked at) and picks the head
- * grouping and the split count.  Heads per workgroup: the largest multiple
- * of 16 that divides H, at most 64, for which B * S * head_groups >= 256
- * (one workgroup per compute unit), else 16; S is chosen for each candidate
- * grouping as below.  num_splits = 0 lets the selector choose:
+ * grouping and the split count.  Heads per workgroup (a multiple of 16 that
+ * divides H, at most 64), with S chosen for each candidate grouping as
+ * below: when the selector chooses S, the smallest grouping whose S >= 2
+ * fills the chip (B * S * head_groups >= 256, one workgroup per compute
+ * unit) with at most 8 tiles of 32 entries per split; otherwise the largest
+ * grouping that fills the chip, else 16.  num_splits = 0 lets the selector
+ * choose:
  *   B >= 256                 -> 1 (one workgroup per token already fills the
  *                               chip; SGLang PR #26383 page, implementation
  *                               item 3: no split-K at >= 256 tokens);

@@ -82,11 +82,8 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         return fail(DSV4_ERR_INVALID_ARGUMENT, "topk_idx_stride %lld < topk + swa %lld",
                     (long long)idx_stride, (long long)kt);
 
-    // Heads per workgroup: a multiple of 16 that divides H, at most 64.  The
-    // largest such group is tried first; while the grid (B x S x groups)
-    // would leave CUs idle, the next smaller group is used, since a small
-    // grid's time is its per-workgroup latency and fewer heads per
-    // workgroup shorten every tile step.
+    // Heads per workgroup: a multiple of 16 that divides H, at most 64 (see
+    // below for the choice between more head groups and more splits).
     if (num_splits != 0 && (num_splits < 1 || num_splits > kMaxSplits))
         return fail(DSV4_ERR_INVALID_ARGUMENT, "num_splits must be 0 (auto) or in [1, %d] (got %d)",
                     kMaxSplits, num_splits);
@@ -100,13 +97,33 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         if (want < 1) want = 1;
         return (int)want;
     };
+    // With the split count left to the selector, the smallest group whose
+    // splits fill the chip while each split keeps at most kMaxSplitTiles tiles
+    // wins: smaller groups reach the chip with fewer splits, so less partial
+    // traffic.  Otherwise (no such group, or a forced split count) the
+    // largest group that fills the chip, else 16.
     int hg = 0, groups = 0, S = 0;
-    for (int cand = kMaxHeadsPerGroup; cand >= 16; cand -= 16) {
-        if (d->num_heads % cand) continue;
-        hg = cand;
-        groups = d->num_heads / cand;
-        S = pick_splits(groups);
-        if ((int64_t)d->batch * S * groups >= kCUs) break;
+    if (num_splits == 0) {
+        for (int cand = 16; cand <= kMaxHeadsPerGroup; cand += 16) {
+            if (d->num_heads % cand) continue;
+            const int g = d->num_heads / cand, sc = pick_splits(g);
+            const int64_t tiles = ceil_div(ceil_div(kt, sc), kTile);
+            if (sc >= 2 && tiles <= kMaxSplitTiles && (int64_t)d->batch * sc * g >= kCUs) {
+                hg = cand;
+                groups = g;
+                S = sc;
+                break;
+            }
+        }
+    }
+    if (hg == 0) {
+        for (int cand = kMaxHeadsPerGroup; cand >= 16; cand -= 16) {
+            if (d->num_heads % cand) continue;
+            hg = cand;
+            groups = d->num_heads / cand;
+            S = pick_splits(groups);
+            if ((int64_t)d->batch * S * groups >= kCUs) break;
+        }
     }
     const int64_t units = (int64_t)d->batch * S;
     const int64_t grid = ceil_div(units, kXcds) * kXcds * groups;

@@ -23,6 +23,7 @@ constexpr int kThreads = 512;
 constexpr int kTile = 32;
 constexpr int kMaxHeadsPerGroup = 64;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxSplitTiles = 8;   // selector: tiles per split before larger head groups win
 constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin
 constexpr int kCombineThreads = 128;  // 4 output dims per thread

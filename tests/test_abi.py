@@ -101,8 +101,17 @@ def _expected_splits(B, groups, Kt, forced):
 
 
 def _expected_plan(B, H, Kt, forced=0):
-    """(heads_per_group, splits): the largest of 64/48/32/16 dividing H whose
-    grid B * S * groups reaches 256 workgroups, else 16."""
+    """(heads_per_group, splits).  Selector splits: the smallest of
+    16/32/48/64 dividing H whose splits (>= 2) fill 256 workgroups with at
+    most 8 tiles of 32 entries each.  Otherwise the largest group whose grid
+    B * S * groups reaches 256 workgroups, else 16."""
+    if not forced:
+        for hg in (16, 32, 48, 64):
+            if H % hg:
+                continue
+            S = _expected_splits(B, H // hg, Kt, 0)
+            if S >= 2 and -(-(-(-Kt // S)) // 32) <= 8 and B * S * (H // hg) >= 256:
+                return hg, S
     for hg in (64, 48, 32, 16):
         if H % hg:
             continue
@@ -281,3 +290,12 @@ def test_dual_cache_validation_without_touching_the_gpu():
     assert call(pool(kv=None), pool()) == E
     assert call(pool(), pool(), q=None) == E
     assert "swa pool" in (call(pool(), pool(nb=0)) == E and dsv4.dsv4_last_error())
+
+
+@pytest.mark.parametrize("B,hg,S", [(1, 16, 32), (2, 16, 32), (4, 16, 16), (8, 16, 8),
+                                     (16, 32, 8), (32, 64, 8), (64, 64, 4), (256, 64, 1)])
+def test_selector_on_the_headline_shape_across_batch_sizes(B, hg, S):
+    """H=64, top-k 2048: the groupings a batch sweep on the GPU measured
+    fastest (B = 4, 8, 16 gain 10-24 % over the largest filling group)."""
+    p = dsv4.dsv4_sparse_decode_plan(_desc(B, 64, 2048, 0), 0)
+    assert (p.heads_per_group, p.num_splits) == (hg, S) == _expected_plan(B, 64, 2048)
