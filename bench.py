@@ -59,6 +59,10 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to defeat the caches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-workload", type=int, default=None, metavar="CI",
+                    help="instead of the benchmark: run the selector's decode of workload CI "
+                         "(0-4) --steps times, for counter passes, and print its algorithmic "
+                         "work as JSON")
     ap.add_argument("--no-two-kernel", action="store_true",
                     help="skip the fused vs two-kernel comparison on the large-batch workload")
     ap.add_argument("--scrub", action="store_true",
@@ -97,6 +101,8 @@ def _traffic_from_profile(digest: str):
 
 def main() -> int:
     args = _parse()
+    if args.profile_workload is not None:
+        return profile_workload(args.profile_workload, args.steps)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode path "
               "is single-GPU; see DESIGN.md for how it would shard.", file=sys.stderr)
@@ -394,6 +400,40 @@ def main() -> int:
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, out, lse, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+    return 0
+
+
+def profile_workload(ci: int, steps: int) -> int:
+    """Runs the fused decode of one of the five workloads `steps` times,
+    launch after launch, so that a profiler's counters can be averaged per
+    dispatch; prints the valid entries and algorithmic flops of one call."""
+    import torch
+    import sparse_mla_attention_block_amd as dsv4
+    from synth import make_workload
+    w = make_workload(ci)
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev) if a is not None else None
+    q = t(w.q.view(np.int16)).view(torch.bfloat16)
+    kv, bt, idx, vl, sink = t(w.kv), t(w.block_table), t(w.topk_idx), t(w.valid_len), t(w.sink)
+    out = torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    dk = dict(batch=w.B, num_heads=w.H, topk=w.topk, swa=w.swa, block_size=w.block_size,
+              num_blocks=w.num_blocks, page_stride=w.page_stride, sm_scale=w.sm_scale,
+              max_blocks_per_seq=w.max_blocks_per_seq, block_table_stride=w.block_table.shape[1])
+    plan = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**dk), w.num_splits)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    desc = dsv4.make_desc(workspace=ws, **dk)
+    for _ in range(steps):
+        dsv4.dsv4_sparse_decode(desc, q, kv, bt, idx, vl, sink, out, lse, w.num_splits)
+    torch.cuda.synchronize()
+    n_valid = 0
+    for b in range(w.B):
+        v = w.topk if w.valid_len is None else min(max(int(w.valid_len[b]), 0), w.topk)
+        n_valid += int((w.topk_idx[b, :v] >= 0).sum() + (w.topk_idx[b, w.topk:] >= 0).sum())
+    print(json.dumps({"workload": w.name, "valid_entries": n_valid,
+                      "algorithmic_flops": n_valid * 2048 * w.H,
+                      "heads_per_group": plan.heads_per_group, "num_splits": plan.num_splits,
+                      "launches": steps}), flush=True)
     return 0
 
 
