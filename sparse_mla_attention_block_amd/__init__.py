@@ -1,8 +1,9 @@
 """Python binding of libdsv4.so, the MI355X sparse FP8 MLA decode library.
 
-Argument marshalling only: every function here has the name of a C entry
-point in include/dsv4.h, turns torch tensors into device pointers and calls
-it through ctypes.  Every step of the path runs in the HIP kernels; there is
+Argument marshalling only: each dsv4_* function here has the name of a C
+entry point in include/dsv4.h, turns torch tensors into device pointers and
+calls it through ctypes; make_desc, make_pool and workspace_split_views only
+fill the ABI's structs or view a workspace.  Every step of the path runs in the HIP kernels; there is
 no CPU or PyTorch fallback.  If the library has not been built, importing
 this package fails.
 """

@@ -1,5 +1,6 @@
 // Sparse FP8 MLA decode kernels for gfx950 (CDNA4): the partial (split-K)
-// kernel and the log-sum-exp combine kernel.
+// kernel, the log-sum-exp combine kernel, the two-kernel path's gather and
+// dense-source kernels, and the gather-floor measurement kernel.
 //
 // Method sources (page titles):
 //   vLLM PR #52212, gfx950 DSV4 sparse decode page, implementation item 1:
@@ -13,7 +14,7 @@
 // One workgroup = 8 waves serves one (token b, split s, head group g) and
 // walks its slice of the token's entry list in tiles of 32 cache rows, as a
 // software pipeline with one barrier per step.  In step t:
-//   * waves 0..3 ("consumers", one per 16-head MFMA tile) run QK of tile t
+//   * waves 0..HG/16-1 ("consumers", one per 16-head MFMA tile) run QK of tile t
 //     on bf16 MFMA 16x16x32 (q held in registers, S^T = K q^T so each lane
 //     holds 8 scores of one head) fused with the online softmax (cross-row
 //     permlane reductions, lazy rescaling: the running max only moves when a
@@ -33,6 +34,10 @@
 // probabilities, the PV operand their bf16 rounding.  With one split the
 // epilogue folds the sink in and writes bf16 output and lse; with several it
 // writes the split's normalised bf16 partial and lse.
+// Variants of the same body: SCRUB zeroes non-finite dequantised elements;
+// DENSE reads already gathered bf16 rows with a mask (two tiles in flight, as
+// a 1 KB row needs 32 registers per producer lane); a dual cache resolves
+// the SWA entries through a second pool, chosen per entry.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
