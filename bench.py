@@ -105,7 +105,7 @@ def main() -> int:
         return profile_workload(args.profile_workload, args.steps)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode path "
-              "is single-GPU; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "is single-GPU, and this benchmark times one GPU.", file=sys.stderr)
         return 2
     import torch
     import sparse_mla_attention_block_amd as dsv4
