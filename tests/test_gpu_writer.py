@@ -135,3 +135,59 @@ def test_written_cache_decodes_like_the_oracle():
     out, lse = gh.gpu_decode(dw, num_splits=3)
     ro, rl, _ = oracle.decode_workload(w, num_splits=3)
     gh.assert_decode_close(out, lse, ro, rl, "decode of a GPU-written cache")
+
+
+def test_writer_and_two_kernel_path_replay_in_one_graph():
+    """A step that writes new rows into the cache, then gathers and attends
+    over them (two-kernel path), captured once and replayed over three
+    batches of new rows; each replay matches the eager bytes of the writer
+    and the oracle's decode of the resulting pool."""
+    from tests import gpu_helpers as gh
+    w = make_custom(B=2, H=32, topk=128, swa=16, seq_lens=[1500, 600], seed=290,
+                    valid_len_range=(60, 128))
+    bs = w.block_size
+    slots = []
+    for b in range(w.B):
+        for s in np.unique(w.topk_idx[b][w.topk_idx[b] >= 0])[:40]:
+            slots.append(int(w.block_table[b, s // bs]) * bs + int(s) % bs)
+    slots = np.array(slots, dtype=np.int64)
+    n = len(slots)
+    dw = gh.DeviceWorkload(w)
+    rows_d = torch.zeros((n, 512), dtype=torch.int16, device="cuda")
+    slots_d = torch.from_numpy(slots).cuda()
+    Kt = w.topk + w.swa
+    dense = torch.empty((w.B, Kt, 512), dtype=torch.bfloat16, device="cuda")
+    mask = torch.empty((w.B, Kt), dtype=torch.uint8, device="cuda")
+    desc = gh.make_desc(w)
+    out = torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+
+    def step():
+        dsv4.dsv4_quantize_store(rows_d, 512, slots_d, n, dw.kv, bs, w.num_blocks, w.page_stride,
+                                 dsv4.DSV4_STORE_SANITIZE)
+        dsv4.dsv4_gather_dequant(desc, dw.kv, dw.bt, dw.idx, dw.vl, dense, mask)
+        dsv4.dsv4_dense_decode(desc, dw.q, dense, mask, dw.sink, out, lse, 1)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    pool = w.kv.copy()
+    for rep in range(3):
+        rows = make_writer_rows(n, seed=291 + rep, specials=False, spread=2)
+        rows_d.copy_(torch.from_numpy(rows.view(np.int16)).cuda())
+        torch.cuda.synchronize()
+        print(f"graph replay {rep}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        pool = oracle.store_rows(pool, rows, slots, block_size=bs, sanitize=True)
+        assert np.array_equal(dw.kv.cpu().numpy(), pool)
+        w.kv = pool
+        ro, rl, _ = oracle.decode_workload(w)
+        gh.assert_decode_close(out.float().double().cpu().numpy(), lse.double().cpu().numpy(),
+                               ro, rl, f"replay {rep}")
