@@ -460,8 +460,10 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     }
     __syncthreads();
 
-    // Online-softmax state of a consumer lane's head, in base-2 units
-    // (replicated over the lane's four 16-lane rows).
+    // Online-softmax state of a consumer lane's head, in base-2 units: the
+    // running max is replicated over the lane's four 16-lane rows; the running
+    // sum is the lane's own share (all rows of a head rescale by the same
+    // factor), summed over the rows once, before the finish.
     float m_run = -INFINITY, l_run = 0.f;
     // PV accumulators: wave w owns output dims [64w, 64w+64).  acc[mt][nt]
     // is a 16-dim x 16-head block of O^T; lane (l16, lg) holds head 16mt + l16
@@ -680,7 +682,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             psum += e;
             pv8[i] = (__bf16)e;
         }
-        l_run = l_run * a + xrow_sum4(psum);
+        l_run = l_run * a + psum;
         m_run = m_use;
         // Slots 8lg .. 8lg+7 of the head's row: entries 4lg + r, then 16 + 4lg + r.
         *reinterpret_cast<bf16x8*>(Pb + (t & 1) * (HG * kPLd) + hc * kPLd + 8 * lg) = pv8;
@@ -786,6 +788,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             __syncthreads();
         }
         if (ntiles > 0) {
+            l_run = xrow_sum4(l_run);
             if (lg == 0) finish();
             pv(ntiles - 1);
             __syncthreads();
