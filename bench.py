@@ -63,6 +63,9 @@ def _parse():
                     help="instead of the benchmark: run the selector's decode of workload CI "
                          "(0-4) --steps times, for counter passes, and print its algorithmic "
                          "work as JSON")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the batch sweep (profiler runs: its launches share the headline "
+                         "kernel's name)")
     ap.add_argument("--no-two-kernel", action="store_true",
                     help="skip the fused vs two-kernel comparison on the large-batch workload")
     ap.add_argument("--scrub", action="store_true",
@@ -289,7 +292,7 @@ def main() -> int:
     # different addresses), the replicas rotated across steps.
     sweep = []
     K2 = min(K, 400)
-    for Bs in (2, 4, 8, 16, 32, 64):
+    for Bs in () if args.no_sweep else (2, 4, 8, 16, 32, 64):
         if 2 * Bs > R:
             break
         dk = dict(batch=Bs, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
