@@ -332,3 +332,30 @@ def test_dual_pool_equals_the_single_pool_it_was_split_from():
     a = oracle.decode_workload(w, num_splits=3)
     b = oracle.decode_workload(w2, num_splits=3)
     assert a[2] == b[2] and np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(seed=st.integers(0, 10 ** 6), B=st.integers(1, 3), H=st.sampled_from([1, 2, 16]),
+       topk=st.integers(1, 48), swa=st.integers(0, 12), bs=st.sampled_from([1, 3, 16, 64]),
+       invalid=st.sampled_from([0.0, 0.2]), masked=st.booleans(), s_q=st.integers(1, 3),
+       split_pool=st.booleans(), splits=st.sampled_from([0, 1, 2, 5]))
+def test_random_workloads_match_sdpa(seed, B, H, topk, swa, bs, invalid, masked, s_q, split_pool,
+                                     splits):
+    """Random small shapes: the oracle's decode (plain, or split and merged)
+    equals torch's fp64 SDPA over the rows rebuilt from the generator's own
+    values, with the sink as an extra key."""
+    rng = np.random.default_rng(seed)
+    seq_lens = [int(x) for x in rng.integers(s_q + 1, 300, size=B)]
+    w = make_custom(B=B, H=H, topk=topk, swa=swa, seq_lens=seq_lens, seed=seed, block_size=bs,
+                    invalid_frac=invalid, valid_len_range=(0, topk) if masked else None,
+                    keep_floats=True, s_q=s_q)
+    if split_pool:
+        w = split_swa_pool(w, block_size=max(1, bs // 2), seed=seed + 1)
+    out, lse, _ = oracle.decode_workload(w, num_splits=splits)
+    ro, rl = sdpa_reference(w)
+    tol = 1e-9 if splits else RTOL
+    np.testing.assert_allclose(out, ro, rtol=tol, atol=1e-11)
+    np.testing.assert_allclose(lse, rl, rtol=tol, atol=1e-11)
