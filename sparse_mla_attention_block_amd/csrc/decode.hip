@@ -394,19 +394,6 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     // producers keep three tiles of raw bytes in it (rr[0..59]).
     uint32_t rr[64];
     float sink_l2 = -INFINITY;                   // consumer lane's sink, base-2 units
-    if (consumer) {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(
-            p.q + ((int64_t)b * p.H + h0 + hc) * kD + 8 * lg);
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const u32x4 v = qp[4 * ks];
-            rr[4 * ks] = v[0];
-            rr[4 * ks + 1] = v[1];
-            rr[4 * ks + 2] = v[2];
-            rr[4 * ks + 3] = v[3];
-        }
-        if (p.sink) sink_l2 = p.sink[h0 + hc] * kLog2e;
-    }
 
     // Resolution of the first 32 tiles (the whole ring): two entries per
     // thread, then a per-tile bit mask of the rows that take part (wave w
@@ -441,6 +428,22 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         }
     }
     __syncthreads();
+
+    // q is loaded only now, beside the producers' first row loads: issued
+    // before the index loads it would hold them back (loads retire in order).
+    if (consumer) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(
+            p.q + ((int64_t)b * p.H + h0 + hc) * kD + 8 * lg);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const u32x4 v = qp[4 * ks];
+            rr[4 * ks] = v[0];
+            rr[4 * ks + 1] = v[1];
+            rr[4 * ks + 2] = v[2];
+            rr[4 * ks + 3] = v[3];
+        }
+        if (p.sink) sink_l2 = p.sink[h0 + hc] * kLog2e;
+    }
 
     if (producer) {
         if constexpr (DENSE) {
