@@ -221,7 +221,11 @@ int dsv4_sparse_decode_partial(const dsv4_decode_desc* desc, const void* q,
  *   D = sum_s e^{part_lse - M} + e^{sink[h] - M},
  *   out[b,h,:] = sum_s e^{part_lse - M} part_out[b,h,s,:] / D  (bf16, RNE),
  *   lse[b,h] = M + ln D.
- * All splits empty: out = 0, lse = sink[h] (or -inf without a sink).
+ * All splits empty: out = 0, lse = sink[h] (or -inf without a sink).  A
+ * split with part_lse = -inf adds nothing, whatever its part_out row holds.
+ * For a given S the result is deterministic; the launch shape (and with it
+ * the order in which splits are added) depends on B*H and S, so results for
+ * different B*H may differ in the last bf16 bit.
  * (SGLang PR #26208 report, implementation item 3: split-K over the top-k
  * axis; vLLM PR #52212 page: the reduce of split partials.)
  *   part_out bf16 [B, H, S, 512] (8-byte aligned), part_lse float [B, H, S],

@@ -142,8 +142,9 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         plan->tile_entries = kTile;
         plan->grid_partial = grid;
         plan->block_partial = kThreads;
-        plan->grid_combine = S > 1 ? (int64_t)d->batch * d->num_heads : 0;
-        plan->block_combine = S > 1 ? kCombineThreads : 0;
+        const dsv4::CombineShape cs = dsv4::combine_shape((int64_t)d->batch * d->num_heads, S);
+        plan->grid_combine = S > 1 ? cs.grid : 0;
+        plan->block_combine = S > 1 ? cs.block : 0;
         plan->workspace_bytes =
             S > 1 ? (size_t)d->batch * d->num_heads * S * (kD * sizeof(uint16_t) + sizeof(float))
                   : 0;

@@ -889,8 +889,8 @@ __global__ __launch_bounds__(kGatherThreads) void gather_dequant_kernel(const De
     if (l8 == 0) mask_out[(int64_t)b * Kt + col] = page >= 0 ? 0 : 1;
 }
 
-// Merge of split partials with the sink; one workgroup per (token, head),
-// 4 output dims per lane.  Splits are taken NB at a time (NB = the split
+// Merge of split partials with the sink for many (token, head) rows; one
+// workgroup per row, 4 output dims per lane.  Splits are taken NB at a time (NB = the split
 // count rounded up to a power of two, at most 32): every partial and lse load
 // of a batch is issued before any is used (one memory round trip per batch),
 // and batches are merged with an online rescale.
@@ -925,9 +925,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
         for (int j = 0; j < kCombineBatch; ++j) {
             const float w = l[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((l[j] - M2) * kLog2e);
             D += w;
-            const f32x4 pv = {__uint_as_float(v[j].x << 16), __uint_as_float(v[j].x & 0xFFFF0000u),
-                              __uint_as_float(v[j].y << 16), __uint_as_float(v[j].y & 0xFFFF0000u)};
-            o += w * pv;
+            if (w != 0.f) {                          // an empty split's row is never read into o
+                const f32x4 pv = {__uint_as_float(v[j].x << 16), __uint_as_float(v[j].x & 0xFFFF0000u),
+                                  __uint_as_float(v[j].y << 16), __uint_as_float(v[j].y & 0xFFFF0000u)};
+                o += w * pv;
+            }
         }
         M = M2;
     }
@@ -943,6 +945,102 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const CombineP
                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o[3]) << 16);
     *reinterpret_cast<uint2*>(p.out + bh * kD + threadIdx.x * 4) = packed;
     if (threadIdx.x == 0 && p.lse) p.lse[bh] = lse;
+}
+
+// Merge of split partials for few (token, head) rows: the row's 512 dims
+// are cut into Q slices of 512/Q dims, one workgroup of W waves per slice,
+// each lane holding 512/(64 Q) dims.  Wave w merges splits w, w + W, ...
+// (at most NSW of them; S <= 64).  Every wave loads the row's S lse values,
+// one per lane, with its partial loads (one memory round trip), and reduces
+// them to the common maximum M (sink included) and the weights
+// e^(lse_s - M); the waves' weighted sums then share one scale and are added
+// in LDS in wave order, so the result is deterministic for a given S.  A
+// split of weight 0 (empty, lse = -inf) adds nothing, whatever its partial
+// holds.
+template <int Q, int W, int NSW>
+__global__ __launch_bounds__(64 * W) void combine_slice_kernel(const CombineParams p) {
+    constexpr int DPL = kD / (Q * 64);           // dims per lane
+    constexpr int WPL = DPL / 2;                 // bf16 pairs per lane
+    static_assert(WPL == 1 || WPL == 2 || WPL == 4, "slice width");
+    static_assert(W * NSW <= 64, "splits beyond one lse per lane");
+    __shared__ float part[W > 1 ? W - 1 : 1][DPL][64];
+    const int64_t bh = blockIdx.x / Q;
+    const int qd = (int)(blockIdx.x % Q);
+    const int h = (int)(bh % p.H);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int S = p.S;
+    const float lraw = p.part_lse[bh * S + min(lane, S - 1)];
+    const uint32_t* po = reinterpret_cast<const uint32_t*>(p.part_o + bh * S * kD + qd * (kD / Q)) +
+                         lane * WPL;
+    // Unconditional loads: splits past S re-read split S - 1 and get weight 0.
+    uint32_t v[NSW][WPL];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+        const uint32_t* src = po + (int64_t)min(wave + W * j, S - 1) * (kD / 2);
+        if constexpr (WPL == 1) {
+            v[j][0] = src[0];
+        } else if constexpr (WPL == 2) {
+            const uint2 t = *reinterpret_cast<const uint2*>(src);
+            v[j][0] = t.x;
+            v[j][1] = t.y;
+        } else {
+            const uint4 t = *reinterpret_cast<const uint4*>(src);
+            v[j][0] = t.x;
+            v[j][1] = t.y;
+            v[j][2] = t.z;
+            v[j][3] = t.w;
+        }
+    }
+    const float sink = p.sink ? p.sink[h] : -INFINITY;
+    const float lv = lane < S ? lraw : -INFINITY;
+    const float M = fmaxf(xrow_max4(row_max16(lv)), sink);
+    const bool live = M != -INFINITY;
+    const float wl = (live && lv != -INFINITY) ? __builtin_amdgcn_exp2f((lv - M) * kLog2e) : 0.f;
+    float o[DPL];
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) o[d] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+        const float w = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), wave + W * j));
+        if (w != 0.f) {
+#pragma unroll
+            for (int k = 0; k < WPL; ++k) {
+                o[2 * k] += w * __uint_as_float(v[j][k] << 16);
+                o[2 * k + 1] += w * __uint_as_float(v[j][k] & 0xFFFF0000u);
+            }
+        }
+    }
+    if constexpr (W > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) part[wave - 1][d][lane] = o[d];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int k = 0; k < W - 1; ++k)
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) o[d] += part[k][d][lane];
+    }
+    float D = xrow_sum4(row_sum16(wl));
+    if (live && sink != -INFINITY) D += __builtin_amdgcn_exp2f((sink - M) * kLog2e);
+    const float inv = live ? 1.f / D : 0.f;
+    uint32_t pk[WPL];
+#pragma unroll
+    for (int k = 0; k < WPL; ++k)
+        pk[k] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(o[2 * k] * inv)) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(o[2 * k + 1] * inv)) << 16);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(p.out + bh * kD + qd * (kD / Q)) + lane * WPL;
+    if constexpr (WPL == 1)
+        dst[0] = pk[0];
+    else if constexpr (WPL == 2)
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+    else
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    if (qd == 0 && lane == 0 && p.lse)
+        p.lse[bh] = live ? M + __builtin_amdgcn_logf(D) * kLn2 : -INFINITY;
 }
 
 // Gather floor: the partial kernel's work units (same grid, same XCD
@@ -1060,8 +1158,32 @@ hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int
                  : launch_partial_variant<false>(p, heads_per_group, g, stream);
 }
 
+template <int Q, int W>
+static void launch_combine_slices(const CombineParams& p, dim3 g, dim3 blk, hipStream_t stream) {
+    const int nsw = (p.S + W - 1) / W;
+    if (nsw <= 2)
+        hipLaunchKernelGGL((combine_slice_kernel<Q, W, 2>), g, blk, 0, stream, p);
+    else if (nsw <= 4)
+        hipLaunchKernelGGL((combine_slice_kernel<Q, W, 4>), g, blk, 0, stream, p);
+    else if (nsw <= 8)
+        hipLaunchKernelGGL((combine_slice_kernel<Q, W, 8>), g, blk, 0, stream, p);
+    else if (nsw <= 16)
+        hipLaunchKernelGGL((combine_slice_kernel<Q, W, 16>), g, blk, 0, stream, p);
+    else
+        hipLaunchKernelGGL((combine_slice_kernel<Q, W, 64 / W>), g, blk, 0, stream, p);
+}
+
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-    const dim3 g((unsigned)((int64_t)p.B * p.H)), blk(kCombineThreads);
+    const CombineShape cs = combine_shape((int64_t)p.B * p.H, p.S);
+    const dim3 g((unsigned)cs.grid), blk((unsigned)cs.block);
+    if (cs.slices == 4 && cs.waves == 4) {
+        launch_combine_slices<4, 4>(p, g, blk, stream);
+        return hipGetLastError();
+    }
+    if (cs.slices == 2 && cs.waves == 2) {
+        launch_combine_slices<2, 2>(p, g, blk, stream);
+        return hipGetLastError();
+    }
     if (p.S <= 4)
         hipLaunchKernelGGL(combine_kernel<4>, g, blk, 0, stream, p);
     else if (p.S <= 8)

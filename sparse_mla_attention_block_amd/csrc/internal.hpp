@@ -26,7 +26,7 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxSplitTiles = 8;   // selector: tiles per split before larger head groups win
 constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin
-constexpr int kCombineThreads = 128;  // 4 output dims per thread
+constexpr int kCombineThreads = 128;  // whole-row combine: 4 output dims per thread
 constexpr int kGatherThreads = 256;   // two-kernel path gather: 32 entries x 8 lanes
 
 // LDS tile geometry.  K tiles are row-major [32][512] bf16 with the 16-byte
@@ -141,6 +141,25 @@ hipError_t launch_dense_partial(const DecodeParams& p, int heads_per_group, int6
                                 hipStream_t stream);
 hipError_t launch_gather_dequant(const DecodeParams& p, uint16_t* kv_out, uint8_t* mask_out,
                                  bool scrub, hipStream_t stream);
+// Launch shape of the split combine.  Few (token, head) rows: each row is
+// cut into `slices` dim ranges, one workgroup of `waves` waves per range,
+// wave w merging splits w, w + waves, ...; this spreads the partial reads
+// over more compute units, each with fewer bytes in flight.  Many rows (or
+// more splits than lanes in a wave): one 128-thread workgroup per row.
+// The thresholds come from timing both kernels on MI355X over B*H from 64
+// to 4096 and S from 4 to 64.
+struct CombineShape {
+    int64_t grid;
+    int32_t block;
+    int32_t slices;     // 0: whole-row kernel
+    int32_t waves;
+};
+inline CombineShape combine_shape(int64_t rows, int32_t S) {
+    if (S > 64 || rows >= 2048) return CombineShape{rows, kCombineThreads, 0, 0};
+    const int q = rows <= 128 ? 4 : 2;
+    return CombineShape{rows * q, 64 * q, q, q};
+}
+
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
 hipError_t launch_quantize_store(const StoreParams& p, hipStream_t stream);

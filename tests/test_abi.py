@@ -135,7 +135,12 @@ def test_plan_of_each_workload(ci):
     assert p.block_partial == 512
     if S > 1:
         assert p.workspace_bytes == c["B"] * c["H"] * S * (512 * 2 + 4)
-        assert p.grid_combine == c["B"] * c["H"]
+        rows = c["B"] * c["H"]
+        # Few rows: 4 (<= 128 rows) or 2 dim slices per row, as many waves
+        # per workgroup; else one 128-thread workgroup per row.
+        q = 4 if rows <= 128 else 2 if rows < 2048 else 1
+        assert p.grid_combine == rows * q
+        assert p.block_combine == (64 * q if q > 1 else 128)
     else:
         assert p.workspace_bytes == 0 and p.grid_combine == 0
     assert p.lds_bytes <= 160 * 1024

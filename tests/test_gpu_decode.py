@@ -337,3 +337,62 @@ def test_multi_token_over_global_slots():
     gh.assert_decode_close(out, lse, ro, rl, "multi-token global slots")
     ro2, rl2, _ = oracle.decode_workload(w, num_splits=2)
     gh.assert_decode_close(out, lse, ro2, rl2, "multi-token global slots vs block table")
+
+
+def _merge_fp64(part_out, part_lse, sink):
+    """The split merge as the C ABI defines it (log-sum-exp with the sink),
+    in fp64 over the bf16 partials as given; empty splits (lse = -inf) drop
+    out whatever their partial rows hold."""
+    B, H, S, _ = part_out.shape
+    out = np.zeros((B, H, 512))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            ls = part_lse[b, h]
+            live = ~np.isneginf(ls)
+            sk = -np.inf if sink is None else float(sink[h])
+            M = max(ls[live].max() if live.any() else -np.inf, sk)
+            if M == -np.inf:
+                continue
+            wts = np.exp(ls[live] - M)
+            D = wts.sum() + (np.exp(sk - M) if sk != -np.inf else 0.0)
+            out[b, h] = (wts[:, None] * part_out[b, h][live]).sum(0) / D
+            lse[b, h] = M + np.log(D)
+    return out, lse
+
+
+# One (token, head) count per combine launch shape: 4 dim slices (<= 128
+# rows), 2 slices (< 2048 rows), one workgroup per row (>= 2048 rows).
+@pytest.mark.parametrize("B,H", [(1, 64), (3, 64), (32, 64)])
+@pytest.mark.parametrize("S", [2, 5, 32, 64])
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_combine_launch_shapes_and_empty_split_contents(B, H, S, with_sink):
+    print(f"combine B={B} H={H} S={S} sink={with_sink}", flush=True)
+    rng = np.random.default_rng(500 + B + S)
+    po = rng.standard_normal((B, H, S, 512)).astype(np.float32)
+    pl = (3.0 * rng.standard_normal((B, H, S))).astype(np.float32)
+    pl[rng.random((B, H, S)) < 0.2] = -np.inf          # empty splits
+    pl[0, 1, :] = -np.inf                              # a row with every split empty
+    sink = rng.standard_normal(H).astype(np.float32) if with_sink else None
+    po_bf = torch.from_numpy(po).to(torch.bfloat16)
+    exact = po_bf.double().numpy()
+    ref_out, ref_lse = _merge_fp64(exact, pl.astype(np.float64), sink)
+    sk = None if sink is None else torch.from_numpy(sink).cuda()
+    runs = []
+    for poison in (False, True):
+        p = po_bf.clone()
+        if poison:                                     # empty splits' rows hold NaN
+            p[torch.from_numpy(np.isneginf(pl))] = float("nan")
+        out = torch.full((B, H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B, H), float("nan"), dtype=torch.float32, device="cuda")
+        dsv4.dsv4_combine_splits(B, H, S, p.cuda(), torch.from_numpy(pl).cuda(), sk, out, lse,
+                                 None)
+        torch.cuda.synchronize()
+        runs.append((out.cpu(), lse.cpu()))
+    gh = _gh()
+    gh.assert_decode_close(runs[0][0].double().numpy(), runs[0][1].double().numpy(),
+                           ref_out, ref_lse, f"combine B={B} H={H} S={S}")
+    assert torch.equal(runs[0][0].view(torch.int16), runs[1][0].view(torch.int16))
+    assert torch.equal(runs[0][1], runs[1][1])
+    assert np.all(runs[0][0][0, 1].float().numpy() == 0.0)
+    assert runs[0][1][0, 1].item() == (float(sink[1]) if with_sink else -np.inf)
