@@ -1,0 +1,102 @@
+"""The oracle against the hand-worked fixtures in tests/golden/ (each cites
+the page passage it follows), and the library's exported constants and plan
+against the format constants the pages print."""
+
+from __future__ import annotations
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import golden_fixtures as gf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _consts():
+    return {c["name"]: c["value"] for c in gf.load("fp8_ds_mla_layout.json")["constants"]}
+
+
+def test_header_constants_match_the_pages():
+    text = open(os.path.join(ROOT, "include", "dsv4.h")).read()
+    defs = dict(re.findall(r"#define (DSV4_\w+) (\d+)\b", text))
+    c = _consts()
+    assert int(defs["DSV4_D_QK"]) == c["D_QK"]
+    assert int(defs["DSV4_D_NOPE"]) == c["D_NOPE"]
+    assert int(defs["DSV4_D_ROPE"]) == c["D_ROPE"]
+    assert c["D_NOPE"] + c["D_ROPE"] == c["D_QK"]
+    assert int(defs["DSV4_ROW_DATA_BYTES"]) == c["ROW_DATA_BYTES"] == c["D_NOPE"] + 2 * c["D_ROPE"]
+    assert int(defs["DSV4_ROW_SCALE_BYTES"]) == c["ROW_SCALE_BYTES"]
+    assert c["D_NOPE"] // c["SCALE_GROUP_DIMS"] == c["ROW_SCALE_BYTES"] - 1
+
+
+def test_plan_tiles_and_split_caps_match_the_pages():
+    import sparse_mla_attention_block_amd as dsv4
+    c = _consts()
+
+    def plan(B, H, topk):
+        d = dsv4.make_desc(batch=B, num_heads=H, topk=topk, swa=0, block_size=64,
+                           num_blocks=1 << 16, page_stride=64 * 584, sm_scale=1.0)
+        return dsv4.dsv4_sparse_decode_plan(d, 0)
+
+    short, long_ = plan(1, 16, 512), plan(1, 16, 8192)
+    assert short.tile_entries == long_.tile_entries == c["TILE_ENTRIES"]
+    assert short.num_splits == c["SPLIT_CAP_SHORT"]          # one token, one head group: capped
+    assert long_.num_splits == c["SPLIT_CAP_LONG"]
+
+
+def test_sanitising_writer_caps_the_scale_code():
+    x = np.zeros(512, dtype=np.uint16)
+    x[5] = 0x7F80                                            # +inf in NoPE group 0
+    _, scales = oracle.quantize_row(x, sanitize=True)
+    assert scales[0] == _consts()["SANITISED_MAX_SCALE_CODE"]
+
+
+@pytest.mark.parametrize("case", ["no_sink", "sink_zero"])
+def test_oracle_reproduces_the_hand_worked_decode(case):
+    fx = gf.load("decode_two_rows.json")
+    inp = gf.decode_inputs(fx)
+    g = inp["geometry"]
+    sink = None if case == "no_sink" else np.zeros(g["H"], dtype=np.float32)
+    out, lse, n = oracle.sparse_decode(
+        q=inp["q"], kv=inp["kv"], topk_idx=inp["topk_idx"], topk=g["topk"], swa=g["swa"],
+        block_size=g["block_size"], num_blocks=g["num_blocks"], page_stride=g["page_stride"],
+        sm_scale=g["sm_scale"], block_table=inp["block_table"],
+        max_blocks_per_seq=inp["max_blocks_per_seq"], sink=sink)
+    ref_out, ref_lse = gf.decode_expected(fx, case)
+    assert n == 2
+    assert np.all(np.isfinite(out))
+    np.testing.assert_allclose(out, ref_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_oracle_dequantises_the_fixture_rows():
+    fx = gf.load("decode_two_rows.json")
+    inp = gf.decode_inputs(fx)
+    g = inp["geometry"]
+    d = oracle.make_desc(B=1, H=g["H"], topk=g["topk"], swa=0, block_size=g["block_size"],
+                         num_blocks=g["num_blocks"], page_stride=g["page_stride"], sm_scale=1.0,
+                         block_table=inp["block_table"])
+    for r in fx["rows"]:
+        assert oracle.resolve(d, inp["block_table"], 0, r["slot"]) == (r["page"], r["offset"])
+        row = oracle.dequant_row(d, inp["kv"], r["page"], r["offset"])
+        groups = [2.0 ** (c - 127) for c in r["scale_codes"]]
+        np.testing.assert_array_equal(row[:448], np.repeat(groups, 64))
+        assert np.all(row[448:] == (0.0 if r["rope_bf16_bits"] == 0 else 0.5))
+    assert oracle.resolve(d, inp["block_table"], 0, -1) is None
+    assert oracle.resolve(d, inp["block_table"], 0, 12) is None      # block 3, past the table
+
+
+@pytest.mark.parametrize("fill", [0, -1])
+def test_oracle_reproduces_the_hand_worked_conversion(fill):
+    fx = gf.load("convert_hand_worked.json")
+    got = oracle.convert_req_index_to_global(
+        token_indices=np.array(fx["token_indices"], dtype=np.int32),
+        block_table=np.array(fx["block_table"], dtype=np.int32),
+        max_blocks_per_req=fx["max_blocks_per_req"], block_size=fx["block_size"],
+        req_id=np.array(fx["req_id"], dtype=np.int32), invalid_fill=fill)
+    want = fx["expected"]["fill_0" if fill == 0 else "fill_minus_1"]
+    np.testing.assert_array_equal(got, np.array(want, dtype=np.int32))
