@@ -66,6 +66,8 @@ def _parse():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the batch sweep (profiler runs: its launches share the headline "
                          "kernel's name)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload decode table (all five seeded workloads)")
     ap.add_argument("--no-two-kernel", action="store_true",
                     help="skip the fused vs two-kernel comparison on the large-batch workload")
     ap.add_argument("--scrub", action="store_true",
@@ -398,6 +400,8 @@ def main() -> int:
         "kernel_source_digest": digest,
     }
 
+    if not args.no_workloads:
+        rec["workloads"] = workloads_leg(dev)
     if not args.no_two_kernel:
         rec["two_kernel_large_batch"] = two_kernel_leg(dev, capture_fn=None)
     if not args.no_cpu_baseline:
@@ -438,6 +442,112 @@ def profile_workload(ci: int, steps: int) -> int:
                       "heads_per_group": plan.heads_per_group, "num_splits": plan.num_splits,
                       "launches": steps}), flush=True)
     return 0
+
+
+def _valid_entries(w) -> int:
+    """Entries that take part: index >= 0, inside valid_len for the main
+    part, and on a page the sequence's block table names."""
+    seq = np.arange(w.B) // w.s_q
+    k = np.arange(w.Kt)[None, :]
+    vl = (np.clip(w.valid_len[seq], 0, w.topk) if w.valid_len is not None
+          else np.full(w.B, w.topk))[:, None]
+    ti = w.topk_idx
+    blk = np.where(ti >= 0, ti // w.block_size, 0)
+    inb = blk < w.max_blocks_per_seq
+    page = w.block_table[seq[:, None], np.where(inb, blk, 0)]
+    live = (ti >= 0) & ((k >= w.topk) | (k < vl)) & inb & (page >= 0) & (page < w.num_blocks)
+    return int(live.sum())
+
+
+def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
+    """The library's decode (partial kernel, then the combine when the plan
+    splits) on each of the five seeded workloads, at the plan the selector
+    picks (the tiny workload forces one split).  Average launch durations
+    from HIP graphs of K decodes: warm (one copy of the cache) and cold (the
+    cache rotated over R replicas, R sized so that the rows read between two
+    uses of a replica exceed twice the Infinity Cache, within
+    pool_cap_bytes; `MB_between_reuse` says how far that got).  Throughput
+    and the roofline fractions use the cold time and the algorithmic work:
+    584 + 4 bytes and 2048*H flops per valid entry, q read, output and lse
+    written."""
+    import torch
+    import sparse_mla_attention_block_amd as dsv4
+    from synth import CONFIGS, make_workload
+    res = []
+    for ci in range(len(CONFIGS)):
+        w = make_workload(ci)
+        B, H, Kt = w.B, w.H, w.Kt
+        nb, stride = w.num_blocks, w.page_stride
+        n_valid = _valid_entries(w)
+        touched = n_valid * (ROW_BYTES + 64)
+        R = max(1, min(math.ceil(2 * INFINITY_CACHE_BYTES / touched),
+                       pool_cap_bytes // (nb * stride), K))
+        base = torch.from_numpy(w.kv).to(dev)
+        pool = torch.empty((R, nb, stride), dtype=torch.uint8, device=dev)
+        pool.copy_(base.unsqueeze(0).expand(R, nb, stride))
+        del base
+        bt0 = torch.from_numpy(w.block_table.astype(np.int64)).to(dev)
+        bts = [torch.where(bt0 >= 0, bt0 + r * nb, -1).to(torch.int32).contiguous()
+               for r in range(R)]
+        idx = torch.from_numpy(w.topk_idx).to(dev)
+        vl = None if w.valid_len is None else torch.from_numpy(w.valid_len).to(dev)
+        q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+        sink = torch.from_numpy(w.sink).to(dev)
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        kw = dict(batch=B, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
+                  num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale,
+                  max_blocks_per_seq=w.max_blocks_per_seq,
+                  block_table_stride=w.block_table.shape[1], tokens_per_seq=w.s_q)
+        plan = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**kw), w.num_splits)
+        ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+              if plan.workspace_bytes else None)
+        desc = dsv4.make_desc(workspace=ws, **kw)
+        kv = pool.view(-1)
+
+        def decode(r):
+            dsv4.dsv4_sparse_decode(desc, q, kv, bts[r], idx, vl, sink, out, lse,
+                                    w.num_splits)
+
+        def timed(rot):
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                decode(0)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(K):
+                    decode(i % R if rot else 0)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / K * 1e3
+
+        warm_us = timed(False)
+        cold_us = timed(True)
+        nbytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * (512 * 2 * 2 + 4)
+        flops = n_valid * 2048 * H
+        gbps = nbytes / (cold_us * 1e-6) / 1e9
+        tflops = flops / (cold_us * 1e-6) / 1e12
+        res.append({
+            "workload": w.name, "B": B, "H": H, "topk": w.topk, "swa": w.swa,
+            "valid_entries": n_valid, "heads_per_group": plan.heads_per_group,
+            "num_splits": plan.num_splits, "grid_partial": plan.grid_partial,
+            "replicas": R, "MB_between_reuse": round(R * touched / 1e6, 1),
+            "warm_us": warm_us, "cold_us": cold_us,
+            "tokens_per_s": n_valid / (cold_us * 1e-6),
+            "algorithmic_bytes": nbytes, "GBps": gbps, "frac_hbm": gbps / HBM_PEAK_GBPS,
+            "TFLOPs": tflops, "frac_mfma": tflops / BF16_PEAK_TFLOPS,
+        })
+        del pool, bts, ws, kv
+        torch.cuda.empty_cache()
+    return res
 
 
 def two_kernel_leg(dev, capture_fn=None, K=50):
