@@ -135,17 +135,20 @@ typedef struct dsv4_plan {
  * grouping and the split count.  Heads per workgroup (a multiple of 16 that
  * divides H, at most 64), with S chosen for each candidate grouping as
  * below: when the selector chooses S, the smallest grouping whose S >= 2
- * fills the chip (B * S * head_groups >= 256, one workgroup per compute
- * unit) with at most 8 tiles of 32 entries per split; otherwise the largest
- * grouping that fills the chip, else 16.  num_splits = 0 lets the selector
- * choose:
+ * fills the chip (one more split would take B * (want + 1) * head_groups
+ * past 256 workgroups, one per compute unit) with at most 8 tiles of 32
+ * entries per split; otherwise the largest grouping that fills the chip,
+ * else 16 (with a forced S: B * S * head_groups >= 256).  num_splits = 0
+ * lets the selector choose:
  *   B >= 256                 -> 1 (one workgroup per token already fills the
  *                               chip; SGLang PR #26383 page, implementation
  *                               item 3: no split-K at >= 256 tokens);
- *   otherwise cap = 4 when topk+swa <= 1024 else 32 (vLLM PR #52212 page,
- *   implementation item 2: cap 4 for short work, up to 32 for long context
- *   at low batch), and S = clamp(ceil(256 / (B * head_groups)), 1,
- *   min(cap, ceil((topk+swa)/32))).
+ *   otherwise want = clamp(floor(256 / (B * head_groups)), 1,
+ *   min(32, T)) with T = ceil((topk+swa)/32) tiles (32: the vLLM PR #52212
+ *   page, implementation item 2, cap for long context at low batch; its
+ *   cap of 4 for short work is not applied, as more splits measured faster
+ *   here), and S = ceil(T / ceil(T / want)): the fewest splits with the
+ *   same whole tiles per split, so none is left without entries.
  * A forced num_splits must lie in [1, DSV4_MAX_SPLITS]. */
 int dsv4_sparse_decode_plan(const dsv4_decode_desc* desc, int32_t num_splits, dsv4_plan* plan);
 

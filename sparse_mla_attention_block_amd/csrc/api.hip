@@ -87,15 +87,24 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
     if (num_splits != 0 && (num_splits < 1 || num_splits > kMaxSplits))
         return fail(DSV4_ERR_INVALID_ARGUMENT, "num_splits must be 0 (auto) or in [1, %d] (got %d)",
                     kMaxSplits, num_splits);
-    auto pick_splits = [&](int groups) -> int {
-        if (num_splits != 0) return num_splits;
+    // Selector split count for `groups` head groups.  want: as many splits
+    // as still give every workgroup a compute unit of its own (one partial
+    // workgroup fills a CU's LDS, so a grid past 256 runs a second round),
+    // at most kMaxAutoSplits and at most one per tile; then the fewest
+    // splits with the same tiles per split, so no split is left without
+    // entries (the split chunks are whole tiles).
+    const int64_t tiles = ceil_div(kt, kTile);
+    auto auto_want = [&](int groups) -> int64_t {
         if (d->batch >= 256) return 1;
-        const int64_t cap = kt <= 1024 ? 4 : 32;
-        int64_t want = ceil_div(kCUs, (int64_t)d->batch * groups);
-        const int64_t lim = cap < ceil_div(kt, kTile) ? cap : ceil_div(kt, kTile);
-        if (want > lim) want = lim;
-        if (want < 1) want = 1;
-        return (int)want;
+        int64_t want = kCUs / ((int64_t)d->batch * groups);
+        if (want > kMaxAutoSplits) want = kMaxAutoSplits;
+        if (want > tiles) want = tiles;
+        return want < 1 ? 1 : want;
+    };
+    auto whole_tiles = [&](int64_t want) -> int { return (int)ceil_div(tiles, ceil_div(tiles, want)); };
+    // The grouping fills the chip when one more split would not fit.
+    auto fills = [&](int groups, int64_t want) {
+        return (int64_t)d->batch * groups * (want + 1) > kCUs;
     };
     // With the split count left to the selector, the smallest group whose
     // splits fill the chip while each split keeps at most kMaxSplitTiles tiles
@@ -106,9 +115,11 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
     if (num_splits == 0) {
         for (int cand = 16; cand <= kMaxHeadsPerGroup; cand += 16) {
             if (d->num_heads % cand) continue;
-            const int g = d->num_heads / cand, sc = pick_splits(g);
-            const int64_t tiles = ceil_div(ceil_div(kt, sc), kTile);
-            if (sc >= 2 && tiles <= kMaxSplitTiles && (int64_t)d->batch * sc * g >= kCUs) {
+            const int g = d->num_heads / cand;
+            const int64_t want = auto_want(g);
+            const int sc = whole_tiles(want);
+            const int64_t split_tiles = ceil_div(ceil_div(kt, sc), kTile);
+            if (sc >= 2 && split_tiles <= kMaxSplitTiles && fills(g, want)) {
                 hg = cand;
                 groups = g;
                 S = sc;
@@ -121,8 +132,14 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
             if (d->num_heads % cand) continue;
             hg = cand;
             groups = d->num_heads / cand;
-            S = pick_splits(groups);
-            if ((int64_t)d->batch * S * groups >= kCUs) break;
+            if (num_splits != 0) {
+                S = num_splits;
+                if ((int64_t)d->batch * S * groups >= kCUs) break;
+            } else {
+                const int64_t want = auto_want(groups);
+                S = whole_tiles(want);
+                if (fills(groups, want)) break;
+            }
         }
     }
     const int64_t units = (int64_t)d->batch * S;

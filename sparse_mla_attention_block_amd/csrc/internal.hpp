@@ -23,6 +23,7 @@ constexpr int kThreads = 512;
 constexpr int kTile = 32;
 constexpr int kMaxHeadsPerGroup = 64;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxAutoSplits = 32;  // selector cap (the long-context low-batch cap of the vLLM PR #52212 page)
 constexpr int kMaxSplitTiles = 8;   // selector: tiles per split before larger head groups win
 constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin

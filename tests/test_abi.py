@@ -90,34 +90,51 @@ def _desc(B, H, topk, swa, bs=64, num_blocks=1000, **kw):
     return dsv4.make_desc(**d)
 
 
-def _expected_splits(B, groups, Kt, forced):
-    if forced:
-        return forced
+def _want(B, groups, Kt):
+    """Splits that still give every workgroup its own CU, at most 32 and at
+    most one per 32-entry tile."""
     if B >= 256:
         return 1
-    cap = 4 if Kt <= 1024 else 32
-    want = -(-256 // (B * groups))
-    return max(1, min(want, cap, -(-Kt // 32)))
+    return max(1, min(256 // (B * groups), 32, -(-Kt // 32)))
+
+
+def _whole_tiles(want, Kt):
+    tiles = -(-Kt // 32)
+    return -(-tiles // -(-tiles // want))
+
+
+def _expected_splits(B, groups, Kt, forced):
+    return forced if forced else _whole_tiles(_want(B, groups, Kt), Kt)
 
 
 def _expected_plan(B, H, Kt, forced=0):
     """(heads_per_group, splits).  Selector splits: the smallest of
-    16/32/48/64 dividing H whose splits (>= 2) fill 256 workgroups with at
-    most 8 tiles of 32 entries each.  Otherwise the largest group whose grid
-    B * S * groups reaches 256 workgroups, else 16."""
+    16/32/48/64 dividing H whose splits (>= 2) fill the chip (one more would
+    pass 256 workgroups) with at most 8 tiles of 32 entries each.  Otherwise
+    the largest group that fills the chip (forced S: B * S * groups >= 256),
+    else 16."""
     if not forced:
         for hg in (16, 32, 48, 64):
             if H % hg:
                 continue
-            S = _expected_splits(B, H // hg, Kt, 0)
-            if S >= 2 and -(-(-(-Kt // S)) // 32) <= 8 and B * S * (H // hg) >= 256:
+            g = H // hg
+            want = _want(B, g, Kt)
+            S = _whole_tiles(want, Kt)
+            if S >= 2 and -(-(-(-Kt // S)) // 32) <= 8 and B * g * (want + 1) > 256:
                 return hg, S
     for hg in (64, 48, 32, 16):
         if H % hg:
             continue
-        S = _expected_splits(B, H // hg, Kt, forced)
-        if B * S * (H // hg) >= 256:
-            break
+        g = H // hg
+        if forced:
+            S = forced
+            if B * S * g >= 256:
+                break
+        else:
+            want = _want(B, g, Kt)
+            S = _whole_tiles(want, Kt)
+            if B * g * (want + 1) > 256:
+                break
     return hg, S
 
 
@@ -149,7 +166,7 @@ def test_plan_of_each_workload(ci):
 def test_selector_values_for_the_five_workloads():
     got = [dsv4.dsv4_sparse_decode_plan(_desc(c["B"], c["H"], c["topk"], c["swa"]),
                                         c["num_splits"]).num_splits for c in CONFIGS]
-    assert got == [1, 4, 32, 1, 4]
+    assert got == [1, 10, 32, 1, 4]
 
 
 def test_head_grouping_of_the_five_workloads():
@@ -304,3 +321,19 @@ def test_selector_on_the_headline_shape_across_batch_sizes(B, hg, S):
     fastest (B = 4, 8, 16 gain 10-24 % over the largest filling group)."""
     p = dsv4.dsv4_sparse_decode_plan(_desc(B, 64, 2048, 0), 0)
     assert (p.heads_per_group, p.num_splits) == (hg, S) == _expected_plan(B, 64, 2048)
+
+
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_selector_never_asks_for_a_second_round_of_workgroups(H):
+    """One partial workgroup fills a compute unit: an auto plan keeps
+    B * S * head_groups within the 256 CUs unless B * head_groups alone
+    exceeds them, and each split holds whole tiles with none left empty."""
+    for B in (1, 2, 3, 4, 5, 7, 12, 33, 100, 255, 256, 300):
+        for Kt in (17, 128, 640, 1000, 2048, 2176, 9000):
+            p = dsv4.dsv4_sparse_decode_plan(_desc(B, H, Kt, 0), 0)
+            assert (p.heads_per_group, p.num_splits) == _expected_plan(B, H, Kt)
+            real = B * p.num_splits * p.head_groups
+            assert real <= max(256, B * p.head_groups)
+            tiles = -(-Kt // 32)
+            per = -(-tiles // p.num_splits)
+            assert -(-tiles // per) == p.num_splits          # no split without entries

@@ -44,8 +44,14 @@ def test_plan_tiles_and_split_caps_match_the_pages():
 
     short, long_ = plan(1, 16, 512), plan(1, 16, 8192)
     assert short.tile_entries == long_.tile_entries == c["TILE_ENTRIES"]
-    assert short.num_splits == c["SPLIT_CAP_SHORT"]          # one token, one head group: capped
+    # One token, one head group: the long-context cap binds; the pages' cap
+    # for short work is not applied (the fixture says why): 512 entries
+    # take one split per tile.
     assert long_.num_splits == c["SPLIT_CAP_LONG"]
+    assert short.num_splits == 512 // c["TILE_ENTRIES"] > c["SPLIT_CAP_SHORT"]
+    for B in (1, 2, 3, 5, 8, 64):
+        for topk in (100, 640, 2048, 9000):
+            assert plan(B, 64, topk).num_splits <= c["SPLIT_CAP_LONG"]
 
 
 def test_sanitising_writer_caps_the_scale_code():
