@@ -68,6 +68,8 @@ def _parse():
                          "kernel's name)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the per-workload decode table (all five seeded workloads)")
+    ap.add_argument("--no-context-parallel", action="store_true",
+                    help="skip the one-GPU share of a context-parallel decode")
     ap.add_argument("--no-two-kernel", action="store_true",
                     help="skip the fused vs two-kernel comparison on the large-batch workload")
     ap.add_argument("--scrub", action="store_true",
@@ -402,6 +404,8 @@ def main() -> int:
 
     if not args.no_workloads:
         rec["workloads"] = workloads_leg(dev)
+    if not args.no_context_parallel:
+        rec["context_parallel_share"] = context_parallel_leg(dev, out, lse)
     if not args.no_two_kernel:
         rec["two_kernel_large_batch"] = two_kernel_leg(dev, capture_fn=None)
     if not args.no_cpu_baseline:
@@ -548,6 +552,104 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
         del pool, bts, ws, kv
         torch.cuda.empty_cache()
     return res
+
+
+def context_parallel_leg(dev, full_out, full_lse, K=100, pool_cap_bytes=8 << 30):
+    """One GPU's part of a context-parallel decode of the benchmark workload
+    over n = 2, 4, 8 GPUs: each GPU decodes its share of the index list
+    (topk / n entries, no sink) into a normalised output and lse, the n
+    results are all-gathered (not run: one GPU) and merged with the sink by
+    the combine.  Times: the share's decode, cold over rotating cache
+    replicas and warm; the final combine of n partials.  All n shares are
+    also decoded and merged here, and the merge is compared with the
+    benchmark's own full decode (`max_abs_out_diff_vs_full`)."""
+    import torch
+    import sparse_mla_attention_block_amd as dsv4
+    from synth import make_workload
+    w = make_workload(WORKLOAD_CONFIG)
+    B, H, Kt = w.B, w.H, w.Kt
+    nb, stride = w.num_blocks, w.page_stride
+    n_valid = _valid_entries(w)
+    R = max(1, min(K, pool_cap_bytes // (nb * stride)))
+    base = torch.from_numpy(w.kv).to(dev)
+    pool = torch.empty((R, nb, stride), dtype=torch.uint8, device=dev)
+    pool.copy_(base.unsqueeze(0).expand(R, nb, stride))
+    del base
+    bt0 = torch.from_numpy(w.block_table.astype(np.int64)).to(dev)
+    bts = [torch.where(bt0 >= 0, bt0 + r * nb, -1).to(torch.int32).contiguous() for r in range(R)]
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    sink = torch.from_numpy(w.sink).to(dev)
+    kv = pool.view(-1)
+
+    def graph_us(fn, rot):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                fn(i % R if rot else 0)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K * 1e3
+
+    res = []
+    for n in (2, 4, 8):
+        m = w.topk // n
+        kw = dict(batch=B, num_heads=H, topk=m, swa=0, block_size=w.block_size,
+                  num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale,
+                  max_blocks_per_seq=w.max_blocks_per_seq,
+                  block_table_stride=w.block_table.shape[1], topk_idx_stride=Kt)
+        plan = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**kw), 0)
+        ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+              if plan.workspace_bytes else None)
+        desc = dsv4.make_desc(workspace=ws, **kw)
+        part_out = torch.empty((B, H, n, 512), dtype=torch.bfloat16, device=dev)
+        part_lse = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+        so = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+        sl = torch.empty((B, H), dtype=torch.float32, device=dev)
+        for i in range(n):                        # every share, for the merge check
+            dsv4.dsv4_sparse_decode(desc, q, kv, bts[0], idx[:, i * m:], None, None, so, sl, 0)
+            part_out[:, :, i] = so
+            part_lse[:, :, i] = sl
+        mo = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+        ml = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+        def share(r):
+            dsv4.dsv4_sparse_decode(desc, q, kv, bts[r], idx, None, None, so, sl, 0)
+
+        def merge(r):
+            dsv4.dsv4_combine_splits(B, H, n, part_out, part_lse, sink, mo, ml)
+
+        merge(0)
+        torch.cuda.synchronize()
+        diff = (mo.float() - full_out.float()).abs().max().item()
+        dlse = (ml - full_lse).abs().max().item()
+        cold = graph_us(share, True)
+        warm = graph_us(share, False)
+        comb = graph_us(merge, False)
+        res.append({
+            "gpus": n, "share_entries": m, "heads_per_group": plan.heads_per_group,
+            "num_splits": plan.num_splits, "share_decode_us_cold": cold,
+            "share_decode_us_warm": warm, "final_combine_us": comb,
+            "per_gpu_us_without_exchange": cold + comb,
+            "all_gather_bytes_in_per_gpu": (n - 1) * B * H * (512 * 2 + 4),
+            "max_abs_out_diff_vs_full": diff, "max_abs_lse_diff_vs_full": dlse,
+        })
+        del ws
+    del pool, bts, kv
+    torch.cuda.empty_cache()
+    return {"workload": "long_lowbatch shares: B=1 H=64, topk 2048 cut into n contiguous shares",
+            "replicas": R, "valid_entries_full": n_valid, "shares": res}
 
 
 def two_kernel_leg(dev, capture_fn=None, K=50):
