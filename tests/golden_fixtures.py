@@ -40,7 +40,7 @@ def decode_inputs(fx: dict) -> dict:
 
 
 def decode_expected(fx: dict, case: str):
-    """(out [B, H, 512], lse [B, H]) of the named case ("no_sink" or "sink_zero")."""
+    """(out [B, H, 512], lse [B, H]) of the named case ("no_sink" or "sink_one")."""
     c = fx[case]
     g = fx["geometry"]
     out = np.zeros((g["B"], g["H"], 512))

@@ -61,12 +61,13 @@ def test_sanitising_writer_caps_the_scale_code():
     assert scales[0] == _consts()["SANITISED_MAX_SCALE_CODE"]
 
 
-@pytest.mark.parametrize("case", ["no_sink", "sink_zero"])
+@pytest.mark.parametrize("case", ["no_sink", "sink_one"])
 def test_oracle_reproduces_the_hand_worked_decode(case):
     fx = gf.load("decode_two_rows.json")
     inp = gf.decode_inputs(fx)
     g = inp["geometry"]
-    sink = None if case == "no_sink" else np.zeros(g["H"], dtype=np.float32)
+    sink = (None if case == "no_sink"
+            else np.full(g["H"], fx[case]["sink_value"], dtype=np.float32))
     out, lse, n = oracle.sparse_decode(
         q=inp["q"], kv=inp["kv"], topk_idx=inp["topk_idx"], topk=g["topk"], swa=g["swa"],
         block_size=g["block_size"], num_blocks=g["num_blocks"], page_stride=g["page_stride"],

@@ -1,5 +1,5 @@
 """The HIP path against the hand-worked fixtures in tests/golden/: the
-two-row decode (closed-form outputs and lse, with and without a sink, every
+two-row decode (closed-form outputs and lse, with no sink and with a sink logit of 1, every
 byte of the pool that takes no part is NaN) and the hand-worked conversion
 (bit-exact)."""
 
@@ -15,7 +15,7 @@ from tests import golden_fixtures as gf
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("case", ["no_sink", "sink_zero"])
+@pytest.mark.parametrize("case", ["no_sink", "sink_one"])
 @pytest.mark.parametrize("S", [1, 2])
 def test_hip_decode_reproduces_the_hand_worked_decode(case, S):
     from tests import gpu_helpers as gh
@@ -36,7 +36,8 @@ def test_hip_decode_reproduces_the_hand_worked_decode(case, S):
     kv = torch.from_numpy(inp["kv"]).to(dev)
     bt = torch.from_numpy(inp["block_table"]).to(dev)
     idx = torch.from_numpy(inp["topk_idx"]).to(dev)
-    sink = None if case == "no_sink" else torch.zeros(g["H"], dtype=torch.float32, device=dev)
+    sink = (None if case == "no_sink"
+            else torch.full((g["H"],), fx[case]["sink_value"], dtype=torch.float32, device=dev))
     out = torch.full((g["B"], g["H"], 512), float("nan"), dtype=torch.bfloat16, device=dev)
     lse = torch.full((g["B"], g["H"]), float("nan"), dtype=torch.float32, device=dev)
     dsv4.dsv4_sparse_decode(desc, q, kv, bt, idx, None, sink, out, lse, S)

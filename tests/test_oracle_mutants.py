@@ -19,6 +19,7 @@ from tests import test_oracle_attention as A
 from tests import test_oracle_convert as C
 from tests import test_oracle_decoders as DEC
 from tests import test_oracle_writer as W
+from tests import test_golden as G
 
 MUTANTS = {
     "sink_dropped": ("if (has_sink) D += exp(sink - M);", ""),
@@ -79,10 +80,11 @@ MUTANTS = {
 }
 
 
-def _pins():
-    """Every test function of the pin modules, expanded over its parameters."""
+def _pins(only_golden=False):
+    """Every test function of the pin modules (or of the hand-worked golden
+    fixtures alone), expanded over its parameters."""
     out = []
-    for mod in (DEC, A, C, W):
+    for mod in ((G,) if only_golden else (DEC, A, C, W, G)):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
@@ -130,7 +132,7 @@ for n in ("orc_e4m3fn", "orc_ue8m0", "orc_bf16", "orc_resolve", "orc_dequant_row
     f, g = getattr(mut, n), getattr(real, n)
     f.argtypes, f.restype = g.argtypes, g.restype
 oracle._lib = mut
-for label, fn, kwargs in _pins():
+for label, fn, kwargs in _pins(sys.argv[3] == "golden"):
     try:
         fn(**kwargs)
     except Exception:
@@ -140,13 +142,31 @@ print("PASSED_ALL")
 """
 
 
+def _run_pins(tmp_path, name, which):
+    so = _build_mutant(tmp_path, name, *MUTANTS[name])
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _CHILD, so, root, which], capture_output=True,
+                       text=True, timeout=600)
+    assert "PASSED_ALL" not in r.stdout, f"mutant {name} passed every {which} pin"
+    assert r.returncode != 0 or "CAUGHT" in r.stdout, r.stdout + r.stderr
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_each_mutant_fails_some_pin(name, tmp_path):
     """The pins run in a child process: a mutant that reads out of bounds
     may crash, which also counts as caught (the pin run fails)."""
-    so = _build_mutant(tmp_path, name, *MUTANTS[name])
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    r = subprocess.run([sys.executable, "-c", _CHILD, so, root], capture_output=True, text=True,
-                       timeout=600)
-    assert "PASSED_ALL" not in r.stdout, f"mutant {name} passed every pin"
-    assert r.returncode != 0 or "CAUGHT" in r.stdout, r.stdout + r.stderr
+    _run_pins(tmp_path, name, "all")
+
+
+# Mistakes the hand-worked fixtures of tests/golden/ catch on their own: the
+# row format and scale decoding, the sink and the softmax scale, the lse, the
+# RoPE part of the dot, the conversion, the sanitising writer's code cap.
+GOLDEN_CATCHES = ["sink_dropped", "sink_scaled", "e4m3_bias_8", "ue8m0_bias", "scale_group_63",
+                  "rope_big_endian", "scale_stride_7", "scales_after_row", "lse_without_log",
+                  "dot_skips_rope", "convert_fill_ignored", "convert_offset_dropped",
+                  "convert_no_block_check", "writer_cap_ignores_sanitize"]
+
+
+@pytest.mark.parametrize("name", GOLDEN_CATCHES)
+def test_golden_fixtures_alone_catch(name, tmp_path):
+    _run_pins(tmp_path, name, "golden")
