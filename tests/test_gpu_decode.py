@@ -364,7 +364,7 @@ def _merge_fp64(part_out, part_lse, sink):
 # One (token, head) count per combine launch shape: 4 dim slices (<= 128
 # rows), 2 slices (< 2048 rows), one workgroup per row (>= 2048 rows).
 @pytest.mark.parametrize("B,H", [(1, 64), (3, 64), (32, 64)])
-@pytest.mark.parametrize("S", [1, 2, 3, 5, 32, 64])
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 32, 64, 100])
 @pytest.mark.parametrize("with_sink", [True, False])
 def test_combine_launch_shapes_and_empty_split_contents(B, H, S, with_sink):
     print(f"combine B={B} H={H} S={S} sink={with_sink}", flush=True)
