@@ -86,7 +86,7 @@ def _parse():
 
 def _source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "internal.hpp"):
+    for name in ("decode.hip", "device_util.hpp", "internal.hpp"):
         with open(os.path.join(ROOT, "sparse_mla_attention_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

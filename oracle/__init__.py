@@ -19,6 +19,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB_PATH = os.path.join(HERE, "liboracle.so")
+# A prebuilt oracle library to load instead (e.g. a sanitizer build made by
+# the tests); it is used as is, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("DSV4_ORACLE_LIB")
 
 _lib = None
 
@@ -53,9 +56,11 @@ class OrcDesc(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC):
+        path = _LIB_OVERRIDE or LIB_PATH
+        if not _LIB_OVERRIDE and (not os.path.exists(LIB_PATH)
+                                  or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC)):
             build()
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         L.orc_e4m3fn.argtypes = [ctypes.c_uint8]
         L.orc_e4m3fn.restype = ctypes.c_double

@@ -43,6 +43,7 @@
 
 #include <type_traits>
 
+#include "device_util.hpp"
 #include "internal.hpp"
 
 namespace dsv4 {
@@ -699,8 +700,11 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     auto finish = [&]() __attribute__((always_inline)) {
         const int h = h0 + hc;
         float scale, lse;
-        if (direct && p.sink) {
-            const float M = fmaxf(m_run, sink_l2);
+        const float M = direct && p.sink ? fmaxf(m_run, sink_l2) : -INFINITY;
+        if (M != -INFINITY) {
+            // One split with a sink: fold it into the denominator.  M = -inf
+            // (no entry and a -inf sink) falls through to the empty case
+            // below, since exp2(M - M) would be NaN there.
             const float em = __builtin_amdgcn_exp2f(m_run - M);
             const float D = l_run * em + __builtin_amdgcn_exp2f(sink_l2 - M);
             scale = em * __builtin_amdgcn_rcpf(D);

@@ -16,6 +16,7 @@
 // nontemporal (streaming: 3-6 % faster than cached accesses).
 #include <hip/hip_runtime.h>
 
+#include "device_util.hpp"
 #include "internal.hpp"
 
 namespace dsv4 {

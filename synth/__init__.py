@@ -16,6 +16,7 @@ from .workloads import (  # noqa: F401
     ROW_BYTES,
     Workload,
     make_workload,
+    make_code_sweep,
     make_custom,
     make_writer_rows,
     poison_rows,

@@ -415,3 +415,71 @@ def split_swa_pool(w: Workload, *, block_size: int, seed: int, page_pad: int = 0
     return dataclasses.replace(w, kv=kv1, swa_pool=dict(
         kv=kv2, block_table=bt2, block_size=bs2, num_blocks=pool, page_stride=stride2,
         max_blocks_per_seq=max_blocks))
+
+
+def make_code_sweep(*, seed: int, codes: Sequence[int] = tuple(range(255)), rows_per_code: int = 4,
+                    H: int = 16, block_size: int = 64, decode_safe: bool = False) -> Workload:
+    """A pool that holds every FP8 byte under every given UE8M0 code.
+
+    Token i reads ``rows_per_code`` rows whose seven scale codes all equal
+    codes[i]; each row's 448 NoPE bytes are a seeded shuffle of the byte
+    values 0..255 repeated (every byte appears at least once per row).  The
+    indices are global pool slots (no block table).  RoPE values are
+    bf16(N(0,1)).
+
+    With ``decode_safe`` the rows are fit for attention: the two FP8 NaN
+    bytes (0x7F, 0xFF) become +-0, and under codes where a byte's value times
+    2^(code-127) would reach 2^125 (within a factor 8 of the end of the bf16
+    and fp32 ranges, so that no sum of a few such rows overflows) that byte
+    becomes the largest byte that stays below it, with its sign.  q's NoPE dims are
+    then N(0,1) * 2^(121-code) (zero where that is below the bf16 normal
+    range), so that scores stay of order one at every code, and its RoPE
+    dims N(0,1).  Without it q is bf16(N(0,1)).  Byte magnitudes are read
+    with torch's float8_e4m3fn type (a library decode)."""
+    rng = np.random.default_rng(seed)
+    codes = [int(c) for c in codes]
+    T = len(codes)
+    n_rows = T * rows_per_code
+    mag = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn) \
+        .double().abs().numpy()
+    data = np.empty((n_rows, ROW_DATA_BYTES), dtype=np.uint8)
+    sc = np.zeros((n_rows, ROW_SCALE_BYTES), dtype=np.uint8)
+    base = (np.arange(D_NOPE) % 256).astype(np.uint8)
+    for i, c in enumerate(codes):
+        for k in range(rows_per_code):
+            r = i * rows_per_code + k
+            nope = rng.permutation(base)
+            if decode_safe:
+                nope = np.where((nope & 0x7F) == 0x7F, nope & 0x80, nope)
+                limit = 2.0 ** (252 - c)          # |v| * 2^(c-127) < 2^125
+                ok = np.flatnonzero((mag < limit) & np.isfinite(mag))
+                top = ok[np.argmax(mag[ok])] & 0x7F
+                big = (mag[nope] >= limit) & np.isfinite(mag[nope])
+                nope = np.where(big, (nope & 0x80) | top, nope)
+            data[r, :D_NOPE] = nope
+            data[r, D_NOPE:] = _bf16_bits(rng.standard_normal(D_ROPE, dtype=np.float32)) \
+                .view(np.uint8)
+            sc[r, :7] = c
+    bs = int(block_size)
+    pages = (n_rows + bs - 1) // bs + 1
+    page_stride = bs * ROW_BYTES
+    kv = np.full((pages, page_stride), POISON, dtype=np.uint8)
+    slots = rng.permutation(pages * bs)[:n_rows].astype(np.int64)
+    flat = kv.reshape(-1)
+    page, off = slots // bs, slots % bs
+    d0 = page * page_stride + off * ROW_DATA_BYTES
+    s0 = page * page_stride + bs * ROW_DATA_BYTES + off * ROW_SCALE_BYTES
+    flat[d0[:, None] + np.arange(ROW_DATA_BYTES)[None, :]] = data
+    flat[s0[:, None] + np.arange(ROW_SCALE_BYTES)[None, :]] = sc
+    topk_idx = slots.reshape(T, rows_per_code).astype(np.int32)
+    qf = rng.standard_normal((T, H, D_QK), dtype=np.float32)
+    if decode_safe:
+        e = 121 - np.asarray(codes, dtype=np.float64)
+        s = np.where(e >= -126, np.exp2(np.maximum(e, -126)), 0.0).astype(np.float32)
+        qf[:, :, :D_NOPE] *= s[:, None, None]
+    return Workload(name="code_sweep", seed=seed, B=T, H=H, topk=rows_per_code, swa=0,
+                    block_size=bs, num_blocks=pages, max_blocks_per_seq=0,
+                    page_stride=page_stride, seq_lens=np.full(T, pages * bs, dtype=np.int64),
+                    q=_bf16_bits(qf), kv=kv, block_table=None, topk_idx=topk_idx,
+                    valid_len=None, sink=rng.standard_normal(H).astype(np.float32),
+                    sm_scale=float(np.float32(D_QK ** -0.5)), num_splits=0)

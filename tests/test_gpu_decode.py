@@ -46,6 +46,16 @@ def test_workload_full_size(ci):
     _check(w, f"workload {ci} {w.name}")
 
 
+@pytest.mark.parametrize("S", [4, 2, 3])
+def test_short_batch_at_the_short_work_cap(S):
+    """The short-context batch (B=4, H=64, 512 + 128 entries) at the split
+    counts the pages' short-work cap of 4 allows (vLLM PR #52212 page,
+    implementation item 2), at full size; the selector itself picks more
+    splits for this shape."""
+    w = make_workload(1)
+    _check(w, f"short_batch S={S}", num_splits=S)
+
+
 @pytest.mark.parametrize("S", [1, 2, 3, 7, 32, 64])
 def test_forced_split_counts(S):
     w = make_custom(B=3, H=64, topk=300, swa=37, seq_lens=[5000, 400, 90], seed=10 + S,
