@@ -315,17 +315,21 @@ def poison_rows(w: Workload, b: int, slots: Sequence[int], seed: int, base=None)
     return kv_p, kv_c
 
 
-def make_writer_rows(n: int, seed: int, *, specials: bool = True, spread: int = 30) -> np.ndarray:
+def make_writer_rows(n: int, seed: int, *, specials: bool = True, spread: int = 30,
+                     group_exponents: Optional[np.ndarray] = None) -> np.ndarray:
     """Seeded bf16 rows (uint16 bits [n, 512]) for the cache writer: each
     64-dim NoPE group is N(0,1) times its own power of two drawn from
-    [2^-spread, 2^spread] (at 30 the UE8M0 codes spread over ~60 values),
-    RoPE is N(0,1).  With ``specials``, one row in 8 also gets a special group:
+    [2^-spread, 2^spread] (at 30 the UE8M0 codes spread over ~60 values), or
+    2^group_exponents[row, group] when those are given; RoPE is N(0,1).  With ``specials``, one row in 8 also gets a special group:
     all zeros, a lone +-inf, NaN elements, bf16 subnormals, the bf16 maximum,
     exact E4M3FN ties, +-0 mixtures or values near 2^100, and one row in 16
     a NaN or infinite RoPE value."""
     rng = np.random.default_rng(seed)
     x = np.empty((n, 512), dtype=np.float32)
-    scale = 2.0 ** rng.integers(-spread, spread + 1, size=(n, 7)).astype(np.float32)
+    ex = rng.integers(-spread, spread + 1, size=(n, 7))
+    if group_exponents is not None:
+        ex = np.asarray(group_exponents).reshape(n, 7)
+    scale = 2.0 ** ex.astype(np.float32)
     x[:, :448] = (rng.standard_normal((n, 7, 64)).astype(np.float32) * scale[:, :, None]).reshape(n, 448)
     x[:, 448:] = rng.standard_normal((n, 64)).astype(np.float32)
     bits = _bf16_bits(x)
@@ -427,15 +431,19 @@ def make_code_sweep(*, seed: int, codes: Sequence[int] = tuple(range(255)), rows
     indices are global pool slots (no block table).  RoPE values are
     bf16(N(0,1)).
 
-    With ``decode_safe`` the rows are fit for attention: the two FP8 NaN
-    bytes (0x7F, 0xFF) become +-0, and under codes where a byte's value times
-    2^(code-127) would reach 2^125 (within a factor 8 of the end of the bf16
-    and fp32 ranges, so that no sum of a few such rows overflows) that byte
-    becomes the largest byte that stays below it, with its sign.  q's NoPE dims are
-    then N(0,1) * 2^(121-code) (zero where that is below the bf16 normal
-    range), so that scores stay of order one at every code, and its RoPE
-    dims N(0,1).  Without it q is bf16(N(0,1)).  Byte magnitudes are read
-    with torch's float8_e4m3fn type (a library decode)."""
+    With ``decode_safe`` the rows are fit for attention at the decode
+    tolerance, which is absolute for values of order one: the two FP8 NaN
+    bytes (0x7F, 0xFF) become +-0; bytes of magnitude above 4 have their
+    exponent field lowered by 8 (the same mantissa 256 times smaller), so
+    values lie within +-4 in units of the scale; and under codes where a
+    byte's value times 2^(code-127) would reach 2^125 (within a factor 8 of
+    the end of the bf16 and fp32 ranges, so that no sum of a few such rows
+    overflows) that byte becomes the largest byte that stays below it, with
+    its sign.  q's NoPE dims are then N(0,1) * 2^(127-code), the exponent
+    clipped to [-126, 124] (zero below -126), so that scores stay of order
+    one at every code, and its RoPE dims N(0,1).  Without it q is
+    bf16(N(0,1)).  Byte magnitudes are read with torch's float8_e4m3fn type
+    (a library decode)."""
     rng = np.random.default_rng(seed)
     codes = [int(c) for c in codes]
     T = len(codes)
@@ -451,6 +459,7 @@ def make_code_sweep(*, seed: int, codes: Sequence[int] = tuple(range(255)), rows
             nope = rng.permutation(base)
             if decode_safe:
                 nope = np.where((nope & 0x7F) == 0x7F, nope & 0x80, nope)
+                nope = np.where(mag[nope] > 4.0, nope - 0x40, nope).astype(np.uint8)
                 limit = 2.0 ** (252 - c)          # |v| * 2^(c-127) < 2^125
                 ok = np.flatnonzero((mag < limit) & np.isfinite(mag))
                 top = ok[np.argmax(mag[ok])] & 0x7F
@@ -474,8 +483,8 @@ def make_code_sweep(*, seed: int, codes: Sequence[int] = tuple(range(255)), rows
     topk_idx = slots.reshape(T, rows_per_code).astype(np.int32)
     qf = rng.standard_normal((T, H, D_QK), dtype=np.float32)
     if decode_safe:
-        e = 121 - np.asarray(codes, dtype=np.float64)
-        s = np.where(e >= -126, np.exp2(np.maximum(e, -126)), 0.0).astype(np.float32)
+        e = 127 - np.asarray(codes, dtype=np.float64)
+        s = np.where(e >= -126, np.exp2(np.clip(e, -126, 124)), 0.0).astype(np.float32)
         qf[:, :, :D_NOPE] *= s[:, None, None]
     return Workload(name="code_sweep", seed=seed, B=T, H=H, topk=rows_per_code, swa=0,
                     block_size=bs, num_blocks=pages, max_blocks_per_seq=0,
