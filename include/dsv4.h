@@ -238,6 +238,34 @@ int dsv4_combine_splits(int32_t batch, int32_t num_heads, int32_t num_splits,
                         const void* part_out, const float* part_lse, const float* sink,
                         void* out, float* lse, hipStream_t stream);
 
+/* ----------------------------------------------- allocation-free decode */
+
+/* Bytes of the library's own split-partial scratch (32 MiB per GPU). */
+#define DSV4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* dsv4_sparse_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, but with S > 1 the split
+ * partials go to a fixed device array inside this library instead of
+ * desc->workspace, which is ignored.
+ *   - The array holds DSV4_NOALLOC_SCRATCH_BYTES; a call whose partials
+ *     (dsv4_sparse_decode_workspace_bytes) would not fit returns
+ *     DSV4_ERR_WORKSPACE_TOO_SMALL and launches nothing.
+ *   - Each GPU has its own array, loaded with the library's code and kept
+ *     until the process ends.  Its device address is looked up on the first
+ *     call made with that GPU current; stream must belong to the current
+ *     GPU (DSV4_ERR_INVALID_ARGUMENT otherwise).
+ *   - All calls on one GPU share its array, which keeps the last call's
+ *     partials: calls that overlap on one GPU (other streams, other
+ *     threads) race and give undefined results.  Calls ordered on one
+ *     stream are safe.
+ *   - Nothing is allocated or freed; the call never synchronises.
+ * Arguments and everything else as for dsv4_sparse_decode. */
+int dsv4_sparse_decode_noalloc(const dsv4_decode_desc* desc, const void* q, const void* kv_cache,
+                               const int32_t* block_table, const int32_t* topk_idx,
+                               const int32_t* valid_len, const float* sink, void* out, float* lse,
+                               int32_t num_splits, hipStream_t stream);
+
 /* ---------------------------------------------------------- dual cache */
 
 /* One fp8_ds_mla pool: its pages and how a sequence's req-local slots map

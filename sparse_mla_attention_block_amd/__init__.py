@@ -109,7 +109,8 @@ _lib.dsv4_sparse_decode_plan.argtypes = [_DESC, ctypes.c_int32, ctypes.POINTER(d
 _lib.dsv4_sparse_decode_plan.restype = ctypes.c_int
 _lib.dsv4_sparse_decode_workspace_bytes.argtypes = [_DESC, ctypes.c_int32]
 _lib.dsv4_sparse_decode_workspace_bytes.restype = ctypes.c_size_t
-for _name in ("dsv4_sparse_decode", "dsv4_sparse_decode_partial"):
+NOALLOC_SCRATCH_BYTES = 32 << 20
+for _name in ("dsv4_sparse_decode", "dsv4_sparse_decode_partial", "dsv4_sparse_decode_noalloc"):
     _f = getattr(_lib, _name)
     _f.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]
     _f.restype = ctypes.c_int
@@ -207,6 +208,17 @@ def dsv4_sparse_decode(desc: dsv4_decode_desc, q: torch.Tensor, kv_cache: torch.
     _check(_lib.dsv4_sparse_decode(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table),
                                    _ptr(topk_idx), _ptr(valid_len), _ptr(sink), _ptr(out),
                                    _ptr(lse), num_splits, _stream(stream)))
+
+
+def dsv4_sparse_decode_noalloc(desc: dsv4_decode_desc, q: torch.Tensor, kv_cache: torch.Tensor,
+                               block_table: Optional[torch.Tensor], topk_idx: torch.Tensor,
+                               valid_len: Optional[torch.Tensor], sink: Optional[torch.Tensor],
+                               out: torch.Tensor, lse: Optional[torch.Tensor], num_splits: int = 0,
+                               stream=None) -> None:
+    _check(_lib.dsv4_sparse_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(kv_cache),
+                                           _ptr(block_table), _ptr(topk_idx), _ptr(valid_len),
+                                           _ptr(sink), _ptr(out), _ptr(lse), num_splits,
+                                           _stream(stream)))
 
 
 def dsv4_sparse_decode_partial(desc: dsv4_decode_desc, q: torch.Tensor, kv_cache: torch.Tensor,

@@ -18,14 +18,19 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int status, const char* fmt, ...) {
+int vfail(int status, const char* fmt, va_list ap) {
     char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
     g_last_error = buf;
     return status;
+}
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    const int r = vfail(status, fmt, ap);
+    va_end(ap);
+    return r;
 }
 
 int ok() {
@@ -302,6 +307,16 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
 }
 
 }  // namespace
+
+namespace dsv4 {
+int set_last_error(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    const int r = vfail(status, fmt, ap);
+    va_end(ap);
+    return r;
+}
+}  // namespace dsv4
 
 extern "C" {
 

@@ -150,6 +150,10 @@ inline CombineShape combine_shape(int64_t rows, int32_t S) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+// Records `status` and a printf-style message as the calling thread's last
+// error (dsv4_last_error) and returns `status`.
+int set_last_error(int status, const char* fmt, ...);
 hipError_t launch_convert(const ConvertParams& p, hipStream_t stream);
 hipError_t launch_quantize_store(const StoreParams& p, hipStream_t stream);
 hipError_t launch_gather_floor(const DecodeParams& p, int64_t grid, uint32_t* words,
