@@ -375,8 +375,9 @@ def main() -> int:
         "achieved_hbm_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"decode_partial_kernel<{plan.heads_per_group}, "
-                      f"{'true' if args.scrub else 'false'}>",
+            "kernel": ("decode_short_kernel" if plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT
+                       else "decode_partial_kernel")
+                      + f"<{plan.heads_per_group}, {'true' if args.scrub else 'false'}>",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -507,13 +508,14 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
         ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
               if plan.workspace_bytes else None)
         desc = dsv4.make_desc(workspace=ws, **kw)
+        desc_pipe = dsv4.make_desc(workspace=ws, flags=dsv4.DSV4_DECODE_PIPELINED, **kw)
         kv = pool.view(-1)
 
-        def decode(r):
-            dsv4.dsv4_sparse_decode(desc, q, kv, bts[r], idx, vl, sink, out, lse,
-                                    w.num_splits)
+        def timed(rot, d=desc):
+            def decode(r):
+                dsv4.dsv4_sparse_decode(d, q, kv, bts[r], idx, vl, sink, out, lse,
+                                        w.num_splits)
 
-        def timed(rot):
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s):
@@ -535,6 +537,9 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
 
         warm_us = timed(False)
         cold_us = timed(True)
+        short = plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT
+        pipe = {"pipelined_warm_us": timed(False, desc_pipe),
+                "pipelined_cold_us": timed(True, desc_pipe)} if short else {}
         nbytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * (512 * 2 * 2 + 4)
         flops = n_valid * 2048 * H
         gbps = nbytes / (cold_us * 1e-6) / 1e9
@@ -543,6 +548,7 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
             "workload": w.name, "B": B, "H": H, "topk": w.topk, "swa": w.swa,
             "valid_entries": n_valid, "heads_per_group": plan.heads_per_group,
             "num_splits": plan.num_splits, "grid_partial": plan.grid_partial,
+            "partial_kernel": "short" if short else "pipelined", **pipe,
             "replicas": R, "MB_between_reuse": round(R * touched / 1e6, 1),
             "warm_us": warm_us, "cold_us": cold_us,
             "tokens_per_s": n_valid / (cold_us * 1e-6),

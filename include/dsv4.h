@@ -84,6 +84,11 @@ const char* dsv4_last_error(void);
  * the choice on a flag.)  Other bits are reserved and must be 0. */
 #define DSV4_DECODE_SCRUB 0x1u
 
+/* DSV4_DECODE_PIPELINED: run the pipelined partial kernel even where the plan
+ * would pick the short-split kernel (splits of at most 128 entries); results
+ * differ only by rounding.  For comparing the two kernels. */
+#define DSV4_DECODE_PIPELINED 0x2u
+
 /* Provenance gate: the decode flags a cache of this provenance needs.
  * Returns 0 (the scrub may be skipped) only when every condition holds:
  * the cache is in the fp8_ds_mla format, no KV transfer (another engine,
@@ -128,7 +133,17 @@ typedef struct dsv4_plan {
     int32_t block_combine;       /* threads per combine workgroup                    */
     size_t workspace_bytes;      /* scratch the call needs (0 if S == 1)             */
     size_t lds_bytes;            /* LDS per partial workgroup                        */
+    int32_t partial_kernel;      /* DSV4_KERNEL_PIPELINED or DSV4_KERNEL_SHORT       */
 } dsv4_plan;
+
+/* Partial kernels (dsv4_plan.partial_kernel).  The short-split kernel serves
+ * plans whose splits hold at most 128 entries with 16, 32 or 64 heads per
+ * workgroup: every phase of its one or two 64-row super-tiles runs on all
+ * eight waves, for the latency-bound low-batch regime (vLLM PR #52212 page,
+ * motivation and implementation item 2).  The pipelined kernel streams
+ * longer splits in 32-row tiles. */
+#define DSV4_KERNEL_PIPELINED 0
+#define DSV4_KERNEL_SHORT 1
 
 /* Plan a decode without launching anything: validates the descriptor
  * (pointers other than workspace are not looked at) and picks the head

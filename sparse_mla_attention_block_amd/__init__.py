@@ -33,6 +33,9 @@ DSV4_ERR_WORKSPACE_TOO_SMALL = 3
 DSV4_ERR_HIP = 4
 MAX_SPLITS = 64
 DSV4_DECODE_SCRUB = 0x1
+DSV4_DECODE_PIPELINED = 0x2
+DSV4_KERNEL_PIPELINED = 0
+DSV4_KERNEL_SHORT = 1
 DSV4_STORE_SANITIZE = 0x1
 
 
@@ -93,6 +96,7 @@ class dsv4_plan(ctypes.Structure):
         ("block_combine", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
         ("lds_bytes", ctypes.c_size_t),
+        ("partial_kernel", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

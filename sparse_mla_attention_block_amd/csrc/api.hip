@@ -46,6 +46,7 @@ struct Shape {
     int hg;       // heads per workgroup
     int groups;   // head groups
     int splits;   // S
+    bool short_kernel;
     int64_t kt;   // topk + swa
     int64_t idx_stride;
 };
@@ -79,9 +80,10 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         return fail(DSV4_ERR_INVALID_ARGUMENT,
                     "tokens_per_seq must be >= 0 and divide batch (got %d for batch %d)",
                     d->tokens_per_seq, d->batch);
-    if (d->flags & ~DSV4_DECODE_SCRUB)
+    const uint32_t known = DSV4_DECODE_SCRUB | DSV4_DECODE_PIPELINED;
+    if (d->flags & ~known)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "unknown decode flags 0x%x",
-                    (unsigned)(d->flags & ~DSV4_DECODE_SCRUB));
+                    (unsigned)(d->flags & ~known));
     const int64_t idx_stride = d->topk_idx_stride == 0 ? kt : d->topk_idx_stride;
     if (idx_stride < kt)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "topk_idx_stride %lld < topk + swa %lld",
@@ -151,9 +153,15 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
     const int64_t grid = ceil_div(units, kXcds) * kXcds * groups;
     if (grid > INT32_MAX) return fail(DSV4_ERR_INVALID_ARGUMENT, "grid too large");
 
+    // The short-split kernel takes splits of at most kShortMaxEntries entries
+    // (chunks are whole tiles, as in the kernels) with 16, 32 or 64 heads.
+    const int64_t chunk_max = ceil_div(ceil_div(kt, S), kTile) * kTile;
+    const bool short_kernel = chunk_max <= kShortMaxEntries && (hg == 16 || hg == 32 || hg == 64) &&
+                              !(d->flags & DSV4_DECODE_PIPELINED);
     sh->hg = hg;
     sh->groups = groups;
     sh->splits = S;
+    sh->short_kernel = short_kernel;
     sh->kt = kt;
     sh->idx_stride = idx_stride;
     if (plan) {
@@ -170,7 +178,8 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         plan->workspace_bytes =
             S > 1 ? (size_t)d->batch * d->num_heads * S * (kD * sizeof(uint16_t) + sizeof(float))
                   : 0;
-        plan->lds_bytes = lds_bytes_for(hg);
+        plan->lds_bytes = short_kernel ? short_lds_bytes(hg) : lds_bytes_for(hg);
+        plan->partial_kernel = short_kernel ? DSV4_KERNEL_SHORT : DSV4_KERNEL_PIPELINED;
     }
     return DSV4_OK;
 }
@@ -241,6 +250,11 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.G = sh.groups;
     p.sq = d->tokens_per_seq > 1 ? d->tokens_per_seq : 1;
     p.qk_scale_log2 = d->sm_scale * 1.4426950408889634f;
+    p.fd_S = dsv4::make_fastdiv((uint32_t)p.S);
+    p.fd_G = dsv4::make_fastdiv((uint32_t)p.G);
+    p.fd_sq = dsv4::make_fastdiv((uint32_t)p.sq);
+    p.fd_bs = dsv4::make_fastdiv((uint32_t)p.bs);
+    p.fd_bs2 = p.fd_bs;
     return p;
 }
 
@@ -287,12 +301,16 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
         p.bt_stride2 = swa_pool->block_table_stride;
         p.page_stride2 = swa_pool->page_stride;
         p.bs2 = swa_pool->block_size;
+        p.fd_bs2 = dsv4::make_fastdiv((uint32_t)p.bs2);
         p.max_blocks2 = swa_pool->block_table ? swa_pool->max_blocks_per_seq : 0;
     }
     (void)hipGetLastError();   // start from a clean error state
-    st = launched(dsv4::launch_decode_partial(p, sh.hg, plan.grid_partial,
-                                                          (d->flags & DSV4_DECODE_SCRUB) != 0,
-                                                          stream), "decode partial");
+    const bool scrub = (d->flags & DSV4_DECODE_SCRUB) != 0;
+    st = sh.short_kernel && !swa_pool
+             ? launched(dsv4::launch_decode_short(p, sh.hg, plan.grid_partial, scrub, stream),
+                        "decode short")
+             : launched(dsv4::launch_decode_partial(p, sh.hg, plan.grid_partial, scrub, stream),
+                        "decode partial");
     if (st || !with_combine || sh.splits == 1) return st;
     dsv4::CombineParams c;
     c.part_o = p.part_o;

@@ -1,0 +1,461 @@
+// Short-split decode kernel for gfx950: one workgroup per (token, split,
+// head group) whose split holds at most 128 entries (two super-tiles of 64
+// cache rows).  It is the latency-bound regime of long-context decode at low
+// batch (vLLM PR #52212 page, motivation: the old split-K path lacked
+// parallelism there; implementation item 2: many splits per row): each
+// workgroup sees only one or two tiles, so instead of a software pipeline
+// every phase of a super-tile runs on all 8 waves at once:
+//   1. every lane resolves one cache row per super-tile itself (index ->
+//      page through the block table -> row address; 8 lanes per row) and
+//      issues that row's loads, for both super-tiles up front, while the QK
+//      waves load q; the rows of super-tile 0 are dequantised into the LDS
+//      K tile (FP8 x 2^(code-127) -> bf16, the gfx950 scaled convert);
+//   2. QK on bf16 MFMA 16x16x32 (S^T = K q^T), the (16-row block, 16-head
+//      block) pairs spread over the 8 waves (with 16 heads, the 512-dim dot
+//      is cut into two halves instead), scores to LDS;
+//   3. mask + softmax: 8 or 16 lanes per head, each holding 4 or 8 scores,
+//      wave reductions over DPP rows; online across the two super-tiles;
+//      bf16 probabilities to LDS in the MFMA's k order;
+//   4. PV on bf16 MFMA, wave w owning output dims [64w, 64w+64), V read from
+//      the K tile through the LDS transpose read.
+// Four barriers per super-tile, no other synchronisation.  The epilogue is
+// the pipelined kernel's: with one split the sink is folded in and bf16
+// output and lse are written, with several the split's normalised bf16
+// partial and its lse.  Rows that take no part read the zero row, so a NaN
+// in the cache never reaches an MFMA.
+//
+// Each workgroup runs this code once, and every launch starts with a cold
+// instruction cache, so the bytes of code a workgroup executes cost about as
+// much time as its memory round trips (measured on MI355X: about one cycle
+// per byte).  The kernel is therefore written for a short instruction
+// stream: 32-bit index arithmetic with launch-time divisors, a K tile with a
+// padded row stride so that every LDS access is a base address plus an
+// immediate offset, the block-table lookup chosen at compile time, and loads
+// that sit outside every branch, so that the compiler can wait for exactly
+// the loads a step needs.  Dual-pool decodes use the pipelined kernel.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "decode_common.hpp"
+#include "device_util.hpp"
+#include "internal.hpp"
+
+namespace dsv4 {
+
+// K tile: 64 rows of 512 bf16 at a stride of 520 elements (1040 bytes).  The
+// 16 rows one QK read spans then start 4 banks apart, and the element offset
+// of (row, dim) is row * 520 + dim.
+constexpr int kShortLd = kD + 8;
+
+template <int HG>
+struct ShortSmem {
+    static constexpr int MT = HG / 16;
+    static constexpr int NS = MT == 1 ? 2 : 1;                   // score planes (k halves)
+    static constexpr int sc_ld = kShortRows + 4;                  // f32 per score row
+    static constexpr int pb_ld = kShortRows + 8;                  // bf16 per probability row
+    static constexpr int kn = 0;                                  // [64][520] bf16
+    static constexpr int sc = kn + kShortRows * kShortLd * 2;     // [NS][HG][sc_ld] f32
+    static constexpr int pb = sc + NS * HG * sc_ld * 4;           // [HG][pb_ld] bf16
+    static constexpr int alpha = pb + HG * pb_ld * 2;             // [HG] f32
+    static constexpr int fin = alpha + HG * 4;                    // [HG] f32
+    static constexpr int valid = fin + HG * 4;                    // [2][64] u8
+    static constexpr int bytes = valid + kShortMaxSuper * kShortRows;
+    static_assert(sc % 16 == 0 && pb % 16 == 0 && valid % 16 == 0, "alignment");
+    static_assert(bytes <= 160 * 1024, "LDS");
+};
+
+size_t short_lds_bytes(int hg) {
+    return hg == 16 ? ShortSmem<16>::bytes : hg == 32 ? ShortSmem<32>::bytes : ShortSmem<64>::bytes;
+}
+
+// Stand-in for a sink when there is none.
+__device__ const float kZeroFloat = 0.f;
+
+// A global-memory (address space 1) view of a pointer, so that a load
+// through it is a global load, counted by vmcnt alone: a select between two
+// pointers of different origins would otherwise make it a flat load, after
+// which the compiler can only wait for all outstanding loads.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* global(const T* ptr) {
+    return (const __attribute__((address_space(1))) T*)ptr;
+}
+
+// Resolution of entry `idx` (-1: no part) of sequence `seq` in two stages,
+// so that the block-table loads of several entries are in flight together:
+// the table word (TABLE: a load, unconditional), then the row addresses
+// (the zero row when the entry takes no part; `live` tells which).  Without
+// a table, idx is a pool slot.
+template <bool TABLE>
+__device__ __forceinline__ int32_t table_word(const DecodeParams& p, uint32_t seq, int32_t idx) {
+    if constexpr (!TABLE) return 0;
+    const uint32_t blk = fdiv(idx >= 0 ? (uint32_t)idx : 0u, p.fd_bs);
+    const bool inb = idx >= 0 && blk < (uint32_t)p.max_blocks;
+    return *global(p.bt + (int64_t)seq * p.bt_stride + (inb ? blk : 0u));
+}
+
+template <bool TABLE>
+__device__ __forceinline__ PatchSrc row_source(const DecodeParams& p, int32_t idx, int32_t word,
+                                               bool& live) {
+    const uint32_t ui = idx >= 0 ? (uint32_t)idx : 0u;
+    const uint32_t blk = fdiv(ui, p.fd_bs);
+    const uint32_t off = ui - blk * p.fd_bs.d;
+    int64_t page;
+    if constexpr (TABLE) {
+        const bool inb = idx >= 0 && blk < (uint32_t)p.max_blocks;
+        page = (inb && word >= 0 && word < p.num_blocks) ? (int64_t)word : -1;
+    } else {
+        page = (idx >= 0 && blk < p.num_blocks) ? (int64_t)blk : -1;
+    }
+    live = page >= 0;
+    const uint8_t* base = p.kv + (live ? page : 0) * p.page_stride;
+    const int64_t z = reinterpret_cast<int64_t>(kZeroRow);
+    const int64_t d = reinterpret_cast<int64_t>(base + off * kRowData);
+    const int64_t s = reinterpret_cast<int64_t>(base + p.fd_bs.d * kRowData + off * kRowScale);
+    return PatchSrc{(gbyte*)(live ? d : z), (gbyte*)(live ? s : z + kRowData)};
+}
+
+// Reductions over groups of N consecutive lanes (N = 8 or 16) of a DPP row.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    if constexpr (N == 16) v = fmaxf(v, dpp<0x140>(v));
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    if constexpr (N == 16) v += dpp<0x140>(v);
+    return v;
+}
+
+// Position of entry e (0..63, a multiple of 4) of a super-tile in the MFMA
+// k order of PV: within each 32-entry k-step, k = 8g + 4h + i holds entry
+// 16h + 4g + i, the order in which the LDS transpose read delivers V.
+__device__ __forceinline__ int k_slot(int e) {
+    return (e & 32) + 8 * ((e >> 2) & 3) + 4 * ((e >> 4) & 1);
+}
+
+// Dequantised row chunks of one lane into the padded K tile.
+template <int O, bool SCRUB>
+__device__ __forceinline__ void store_row(const uint32_t (&rr)[64], int prow, int l8,
+                                          __bf16* Kt) {
+    const uint64_t sw = (uint64_t)rr[O + 19] << 32 | rr[O + 18];
+    __bf16* dst = Kt + prow * kShortLd + 8 * l8;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+        bf16x8 v = dequant8(make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]),
+                            (uint32_t)(sw >> (8 * j)) & 0xFFu);
+        if (SCRUB) {
+            u32x4 w = __builtin_bit_cast(u32x4, v);
+            w = u32x4{scrub_pair(w[0]), scrub_pair(w[1]), scrub_pair(w[2]), scrub_pair(w[3])};
+            v = __builtin_bit_cast(bf16x8, w);
+        }
+        *reinterpret_cast<bf16x8*>(dst + 64 * j) = v;
+    }
+    __bf16* rdst = Kt + prow * kShortLd + kDNope + 4 * l8;
+#pragma unroll
+    for (int j = 7; j < kChunks; ++j) {
+        uint2 raw = make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]);
+        if (SCRUB) raw = make_uint2(scrub_pair(raw.x), scrub_pair(raw.y));
+        *reinterpret_cast<uint2*>(rdst + 32 * (j - 7)) = raw;
+    }
+}
+
+template <int HG, bool SCRUB, bool TABLE>
+__global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodeParams p) {
+    constexpr int MT = HG / 16;
+    static_assert(MT == 1 || MT == 2 || MT == 4, "short kernel head groups: 16, 32, 64");
+    using L = ShortSmem<HG>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[L::bytes];
+    __bf16* Kt = reinterpret_cast<__bf16*>(smem + L::kn);
+    float* Sc = reinterpret_cast<float*>(smem + L::sc);
+    __bf16* Pb = reinterpret_cast<__bf16*>(smem + L::pb);
+    float* alpha_s = reinterpret_cast<float*>(smem + L::alpha);
+    float* fin = reinterpret_cast<float*>(smem + L::fin);
+    uint8_t* vflag = smem + L::valid;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    // Work unit: the pipelined kernel's mapping (head groups of one split
+    // kXcds apart, on one XCD), in 32-bit arithmetic.
+    const uint32_t Lb = blockIdx.x;
+    const uint32_t r8 = Lb / kXcds;
+    const uint32_t gq = fdiv(r8, p.fd_G);
+    const uint32_t g = r8 - gq * (uint32_t)p.G;
+    const uint32_t unit = gq * kXcds + Lb % kXcds;
+    if (unit >= (uint64_t)p.units) return;
+    const uint32_t b = fdiv(unit, p.fd_S);
+    const uint32_t s = unit - b * (uint32_t)p.S;
+    const uint32_t seq = fdiv(b, p.fd_sq);
+    const int h0 = (int)g * HG;
+
+    const int vl = p.valid_len ? min(max(p.valid_len[seq], 0), p.topk) : p.topk;
+    const int eff = vl + p.swa;
+    const int chunk = (int)(fdiv((uint32_t)(eff + p.S - 1), p.fd_S) + kTile - 1) / kTile * kTile;
+    const int lo = min((int)s * chunk, eff);
+    const int hi = min(lo + chunk, eff);
+    const int n = hi - lo;                                   // <= 128 (the plan's bound)
+
+    // 1. Resolution and row loads: lane (prow, l8) serves row prow of each
+    // super-tile.  Index loads first, then q, then the block-table loads,
+    // then the rows; every load is unconditional.
+    const int prow = 8 * wave + (lane >> 4) + 4 * ((lane >> 3) & 1), l8 = lane & 7;
+    const int e0 = lo + prow, e1 = e0 + kShortRows;
+    const int32_t* irow = p.idx + (int64_t)b * p.idx_stride;
+    auto index_at = [&](int pos) -> int32_t {
+        const bool in = pos < hi;
+        const int col = pos < vl ? pos : p.topk + (pos - vl);
+        const int32_t v = *global(irow + (in ? col : 0));
+        return in ? v : -1;
+    };
+    const int32_t i0 = index_at(e0);
+    const int32_t i1 = index_at(e1);
+
+    // QK assignment: 16 heads cut the dot into two k halves (wave w: row
+    // block w&3, half w>>2); 32 heads give each wave one (row block, head
+    // block) pair; 64 heads two row blocks of one head block.
+    constexpr int KSTEPS = MT == 1 ? 8 : 16;
+    constexpr int NRB = MT == 4 ? 2 : 1;
+    const int qk_hb = MT == 1 ? 0 : MT == 2 ? (wave >> 2) : (wave & 3);
+    const int qk_rb0 = MT == 4 ? 2 * (wave >> 2) : (wave & 3);
+    const int qk_k0 = MT == 1 ? KSTEPS * (wave >> 2) : 0;
+    uint32_t qr[4 * KSTEPS];
+    {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(
+            p.q + ((int64_t)b * p.H + h0 + 16 * qk_hb + l16) * kD + 32 * qk_k0 + 8 * lg);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const u32x4 v = qp[4 * ks];
+            qr[4 * ks] = v[0];
+            qr[4 * ks + 1] = v[1];
+            qr[4 * ks + 2] = v[2];
+            qr[4 * ks + 3] = v[3];
+        }
+    }
+
+    // Softmax lanes: TPH lanes per head, EPT entries each.
+    constexpr int TPH = (kThreads / HG) < 16 ? (kThreads / HG) : 16;
+    constexpr int EPT = kShortRows / TPH;
+    const int sm_h = tid / TPH, sm_j = tid % TPH;
+    const bool sm_active = tid < HG * TPH;
+    // The sink is loaded unconditionally here and used in the epilogue.
+    const float sink_raw = *global(p.sink ? p.sink + h0 + (sm_active ? sm_h : 0) : &kZeroFloat);
+
+    // Table words, then the rows of both super-tiles (zero rows past the
+    // split's end), all unconditional.
+    const int32_t w0 = table_word<TABLE>(p, seq, i0);
+    const int32_t w1 = table_word<TABLE>(p, seq, i1);
+    uint32_t rr[64];
+    bool live0, live1;
+    load_patch<0>(row_source<TABLE>(p, i0, w0, live0), l8, rr);
+    load_patch<20>(row_source<TABLE>(p, i1, w1, live1), l8, rr);
+    if (l8 == 0) {
+        vflag[prow] = live0 ? 1 : 0;
+        vflag[kShortRows + prow] = live1 ? 1 : 0;
+    }
+    store_row<0, SCRUB>(rr, prow, l8, Kt);
+    __syncthreads();
+
+    // Online-softmax state of a softmax lane's head (replicated over its TPH
+    // lanes), base-2 units.
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nst = (n + kShortRows - 1) / kShortRows;
+    for (int st = 0; st < nst; ++st) {
+        const int nrows = min(n - st * kShortRows, kShortRows);   // rows that may take part
+
+        // 2. QK: scores of the wave's row block(s) for its head block.
+#pragma unroll
+        for (int j = 0; j < NRB; ++j) {
+            const int rb = qk_rb0 + j;
+            if (16 * rb < nrows) {
+                f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+                const __bf16* krow = Kt + (16 * rb + l16) * kShortLd + 32 * qk_k0 + 8 * lg;
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
+                    const bf16x8 qb = __builtin_bit_cast(
+                        bf16x8, u32x4{qr[4 * ks], qr[4 * ks + 1], qr[4 * ks + 2], qr[4 * ks + 3]});
+                    if (ks & 1)
+                        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb, c1, 0, 0, 0);
+                    else
+                        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb, c0, 0, 0, 0);
+                }
+                // Lane (l16, lg) holds head 16*hb + l16 at rows 16rb + 4lg + r.
+                const int plane = MT == 1 ? (wave >> 2) : 0;
+                *reinterpret_cast<f32x4*>(
+                    Sc + (plane * HG + 16 * qk_hb + l16) * L::sc_ld + 16 * rb + 4 * lg) = c0 + c1;
+            }
+        }
+        __syncthreads();
+
+        // 3. Mask + online softmax of the super-tile.
+        if (sm_active) {
+            const int e = sm_j * EPT;
+            const float* sr = Sc + sm_h * L::sc_ld + e;
+            const uint8_t* vf = vflag + st * kShortRows + e;
+            float xs[EPT];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                float v = sr[i];
+                if constexpr (MT == 1) v += sr[HG * L::sc_ld + i];
+                xs[i] = vf[i] ? v * p.qk_scale_log2 : -INFINITY;
+                mx = fmaxf(mx, xs[i]);
+            }
+            mx = group_max<TPH>(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+            const float a = __builtin_amdgcn_exp2f(m_run - m_sub);   // 0 while nothing was seen
+            float ps = 0.f;
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+#pragma unroll
+            for (int q4 = 0; q4 < EPT / 4; ++q4) {
+                bf16x4 pv4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pe = __builtin_amdgcn_exp2f(xs[4 * q4 + i] - m_sub);
+                    ps += pe;
+                    pv4[i] = (__bf16)pe;
+                }
+                *reinterpret_cast<bf16x4*>(Pb + sm_h * L::pb_ld + k_slot(e + 4 * q4)) = pv4;
+            }
+            ps = group_sum<TPH>(ps);
+            l_run = l_run * a + ps;
+            m_run = m_new;
+            if (sm_j == 0) alpha_s[sm_h] = a;
+        }
+        __syncthreads();
+
+        // 4. PV: O^T += V^T P^T over the super-tile's k-steps.
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float a = alpha_s[16 * mt + l16];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] *= a;
+        }
+        const __bf16* vbase = Kt + (4 * lg + (l16 >> 2)) * kShortLd + 64 * wave + 4 * (l16 & 3);
+        const __bf16* pbase = Pb + l16 * L::pb_ld + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (32 * ks < nrows) {
+                bf16x8 pa[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    pa[mt] = *reinterpret_cast<const bf16x8*>(pbase + 16 * mt * L::pb_ld + 32 * ks);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const __bf16* vp = vbase + 32 * ks * kShortLd + 16 * nt;
+                    const i16x4 v0 = lds_read_tr16(vp);
+                    const i16x4 v1 = lds_read_tr16(vp + 16 * kShortLd);
+                    const bf16x8 vb = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt][nt] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pa[mt], acc[mt][nt], 0, 0, 0);
+                }
+            }
+        }
+        if (st + 1 < nst) {
+            __syncthreads();                           // K tile and P free again
+            store_row<20, SCRUB>(rr, prow, l8, Kt);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: output scale and lse per head (one softmax lane per head).
+    const bool direct = p.S == 1;
+    if (sm_active && sm_j == 0) {
+        const int h = h0 + sm_h;
+        const float sink_l2 = p.sink ? sink_raw * kLog2e : -INFINITY;
+        float scale, lse;
+        const float M = direct && p.sink ? fmaxf(m_run, sink_l2) : -INFINITY;
+        if (M != -INFINITY) {
+            const float em = __builtin_amdgcn_exp2f(m_run - M);
+            const float D = l_run * em + __builtin_amdgcn_exp2f(sink_l2 - M);
+            scale = em * __builtin_amdgcn_rcpf(D);
+            lse = (M + __builtin_amdgcn_logf(D)) * kLn2;
+        } else if (l_run > 0.f) {
+            scale = __builtin_amdgcn_rcpf(l_run);
+            lse = (m_run + __builtin_amdgcn_logf(l_run)) * kLn2;
+        } else {
+            scale = 0.f;
+            lse = -INFINITY;
+        }
+        fin[sm_h] = scale;
+        if (direct) {
+            if (p.lse) p.lse[(int64_t)b * p.H + h] = lse;
+        } else {
+            p.part_lse[((int64_t)b * p.H + h) * p.S + s] = lse;
+        }
+    }
+    __syncthreads();
+
+    uint16_t* dst;
+    int64_t row_stride;
+    if (direct) {
+        dst = p.out + ((int64_t)b * p.H + h0) * kD;
+        row_stride = kD;
+    } else {
+        dst = p.part_o + (((int64_t)b * p.H + h0) * p.S + s) * kD;
+        row_stride = (int64_t)p.S * kD;
+    }
+    uint16_t* obase = dst + l16 * row_stride + 64 * wave + 4 * lg;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const float sc = fin[16 * mt + l16];
+        uint16_t* orow = obase + 16 * mt * row_stride;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (__bf16)(acc[mt][nt][r] * sc);
+            *reinterpret_cast<bf16x4*>(orow + 16 * nt) = o;
+        }
+    }
+}
+
+template <int HG>
+static void launch_short_hg(const DecodeParams& p, dim3 g, bool scrub, hipStream_t stream) {
+    const dim3 blk(kThreads);
+    const bool table = p.bt != nullptr;
+    if (scrub) {
+        if (table)
+            hipLaunchKernelGGL((decode_short_kernel<HG, true, true>), g, blk, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_short_kernel<HG, true, false>), g, blk, 0, stream, p);
+    } else {
+        if (table)
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, true>), g, blk, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, false>), g, blk, 0, stream, p);
+    }
+}
+
+hipError_t launch_decode_short(const DecodeParams& p, int heads_per_group, int64_t grid,
+                               bool scrub, hipStream_t stream) {
+    if (p.kv2 != nullptr) return hipErrorInvalidValue;     // single pool only
+    const dim3 g((unsigned)grid);
+    switch (heads_per_group) {
+        case 16: launch_short_hg<16>(p, g, scrub, stream); break;
+        case 32: launch_short_hg<32>(p, g, scrub, stream); break;
+        case 64: launch_short_hg<64>(p, g, scrub, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dsv4

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace dsv4 {
 
 // Row geometry of the fp8_ds_mla cache (SGLang PR #26208 report, key source
@@ -29,6 +31,12 @@ constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kXcds = 8;            // accelerator dies; workgroups go round-robin
 constexpr int kCombineThreads = 128;  // whole-row combine: 4 output dims per thread
 constexpr int kGatherThreads = 256;   // two-kernel path gather: 32 entries x 8 lanes
+
+// Short-split kernel: splits of at most kShortMaxSuper super-tiles of
+// kShortRows cache rows, every phase on all 8 waves.
+constexpr int kShortRows = 64;
+constexpr int kShortMaxSuper = 2;
+constexpr int kShortMaxEntries = kShortRows * kShortMaxSuper;
 
 // LDS tile geometry.  K tiles are row-major [32][512] bf16 with the 16-byte
 // units of each row permuted (see the kernel); probabilities [HG][40] bf16.
@@ -88,6 +96,9 @@ struct DecodeParams {
     int32_t B, H, topk, swa, bs, max_blocks, S, G;
     int32_t sq;                 // query tokens per sequence (block-table row / valid_len entry)
     float qk_scale_log2;        // sm_scale * log2(e)
+    // Launch-time divisors (the short-split kernel): splits, head groups,
+    // tokens per sequence, and the block sizes of the two pools.
+    FastDiv fd_S, fd_G, fd_sq, fd_bs, fd_bs2;
 };
 
 struct CombineParams {
@@ -126,6 +137,9 @@ struct StoreParams {
 // Kernel launchers (return the launch's hipError_t).
 hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
                                  bool scrub, hipStream_t stream);
+hipError_t launch_decode_short(const DecodeParams& p, int heads_per_group, int64_t grid,
+                               bool scrub, hipStream_t stream);
+size_t short_lds_bytes(int heads_per_group);
 hipError_t launch_dense_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
                                 hipStream_t stream);
 hipError_t launch_gather_dequant(const DecodeParams& p, uint16_t* kv_out, uint8_t* mask_out,

@@ -78,8 +78,26 @@ def test_tokens_per_seq_must_divide_the_batch():
 
 def test_unknown_decode_flags_are_rejected():
     dsv4.dsv4_sparse_decode_plan(_desc(1, 64, 10, 0, flags=dsv4.DSV4_DECODE_SCRUB))
-    assert _status(_desc(1, 64, 10, 0, flags=0x2)) == dsv4.DSV4_ERR_INVALID_ARGUMENT
-    assert "flags" in dsv4.dsv4_last_error()
+    dsv4.dsv4_sparse_decode_plan(_desc(1, 64, 10, 0, flags=dsv4.DSV4_DECODE_PIPELINED))
+    for bad in (0x4, 0x80000000):
+        assert _status(_desc(1, 64, 10, 0, flags=bad)) == dsv4.DSV4_ERR_INVALID_ARGUMENT
+        assert "flags" in dsv4.dsv4_last_error()
+
+
+@pytest.mark.parametrize("ci,kernel", [(0, 1), (1, 1), (2, 1), (3, 0), (4, 0)])
+def test_partial_kernel_of_each_workload(ci, kernel):
+    """Splits of at most 128 entries (4 tiles) with 16, 32 or 64 heads per
+    workgroup run the short-split kernel, longer ones the pipelined kernel;
+    the pipelined flag forces the latter."""
+    c = CONFIGS[ci]
+    d = _desc(c["B"], c["H"], c["topk"], c["swa"])
+    plan = dsv4.dsv4_sparse_decode_plan(d, c["num_splits"])
+    assert plan.partial_kernel == kernel
+    Kt = c["topk"] + c["swa"]
+    chunk = -(-(-(-Kt // plan.num_splits)) // 32) * 32
+    assert (chunk <= 128) == (kernel == dsv4.DSV4_KERNEL_SHORT)
+    d = _desc(c["B"], c["H"], c["topk"], c["swa"], flags=dsv4.DSV4_DECODE_PIPELINED)
+    assert dsv4.dsv4_sparse_decode_plan(d, c["num_splits"]).partial_kernel == 0
 
 
 def _desc(B, H, topk, swa, bs=64, num_blocks=1000, **kw):

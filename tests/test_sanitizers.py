@@ -117,6 +117,12 @@ static void decode_ok(const DecodeParams& p, int hg, int64_t grid) {
 hipError_t launch_decode_partial(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
     decode_ok(p, hg, grid); ++g_launches; return hipSuccess;
 }
+hipError_t launch_decode_short(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
+    decode_ok(p, hg, grid);
+    need(hg == 16 || hg == 32 || hg == 64, "short-kernel head group");
+    ++g_launches; return hipSuccess;
+}
+size_t short_lds_bytes(int) { return 0; }
 hipError_t launch_dense_partial(const DecodeParams& p, int hg, int64_t grid, hipStream_t) {
     decode_ok(p, hg, grid); ++g_launches; return hipSuccess;
 }
