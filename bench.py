@@ -86,7 +86,8 @@ def _parse():
 
 def _source_digest() -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "device_util.hpp", "internal.hpp"):
+    for name in ("decode.hip", "decode_short.hip", "decode_common.hpp",
+                 "device_util.hpp", "fastdiv.hpp", "internal.hpp"):
         with open(os.path.join(ROOT, "sparse_mla_attention_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -377,7 +378,8 @@ def main() -> int:
             "bound": "hbm",
             "kernel": ("decode_short_kernel" if plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT
                        else "decode_partial_kernel")
-                      + f"<{plan.heads_per_group}, {'true' if args.scrub else 'false'}>",
+                      + f"<{plan.heads_per_group}, {'true' if args.scrub else 'false'}"
+                      + (", false>" if plan.partial_kernel else ">"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -537,9 +539,9 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
 
         warm_us = timed(False)
         cold_us = timed(True)
-        short = plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT
+        kname = "short" if plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT else "pipelined"
         pipe = {"pipelined_warm_us": timed(False, desc_pipe),
-                "pipelined_cold_us": timed(True, desc_pipe)} if short else {}
+                "pipelined_cold_us": timed(True, desc_pipe)} if kname != "pipelined" else {}
         nbytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * (512 * 2 * 2 + 4)
         flops = n_valid * 2048 * H
         gbps = nbytes / (cold_us * 1e-6) / 1e9
@@ -548,7 +550,7 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
             "workload": w.name, "B": B, "H": H, "topk": w.topk, "swa": w.swa,
             "valid_entries": n_valid, "heads_per_group": plan.heads_per_group,
             "num_splits": plan.num_splits, "grid_partial": plan.grid_partial,
-            "partial_kernel": "short" if short else "pipelined", **pipe,
+            "partial_kernel": kname, **pipe,
             "replicas": R, "MB_between_reuse": round(R * touched / 1e6, 1),
             "warm_us": warm_us, "cold_us": cold_us,
             "tokens_per_s": n_valid / (cold_us * 1e-6),

@@ -42,11 +42,6 @@
 
 namespace dsv4 {
 
-// K tile: 64 rows of 512 bf16 at a stride of 520 elements (1040 bytes).  The
-// 16 rows one QK read spans then start 4 banks apart, and the element offset
-// of (row, dim) is row * 520 + dim.
-constexpr int kShortLd = kD + 8;
-
 template <int HG>
 struct ShortSmem {
     static constexpr int MT = HG / 16;
@@ -66,103 +61,6 @@ struct ShortSmem {
 
 size_t short_lds_bytes(int hg) {
     return hg == 16 ? ShortSmem<16>::bytes : hg == 32 ? ShortSmem<32>::bytes : ShortSmem<64>::bytes;
-}
-
-// Stand-in for a sink when there is none.
-__device__ const float kZeroFloat = 0.f;
-
-// A global-memory (address space 1) view of a pointer, so that a load
-// through it is a global load, counted by vmcnt alone: a select between two
-// pointers of different origins would otherwise make it a flat load, after
-// which the compiler can only wait for all outstanding loads.
-template <class T>
-__device__ __forceinline__ const __attribute__((address_space(1))) T* global(const T* ptr) {
-    return (const __attribute__((address_space(1))) T*)ptr;
-}
-
-// Resolution of entry `idx` (-1: no part) of sequence `seq` in two stages,
-// so that the block-table loads of several entries are in flight together:
-// the table word (TABLE: a load, unconditional), then the row addresses
-// (the zero row when the entry takes no part; `live` tells which).  Without
-// a table, idx is a pool slot.
-template <bool TABLE>
-__device__ __forceinline__ int32_t table_word(const DecodeParams& p, uint32_t seq, int32_t idx) {
-    if constexpr (!TABLE) return 0;
-    const uint32_t blk = fdiv(idx >= 0 ? (uint32_t)idx : 0u, p.fd_bs);
-    const bool inb = idx >= 0 && blk < (uint32_t)p.max_blocks;
-    return *global(p.bt + (int64_t)seq * p.bt_stride + (inb ? blk : 0u));
-}
-
-template <bool TABLE>
-__device__ __forceinline__ PatchSrc row_source(const DecodeParams& p, int32_t idx, int32_t word,
-                                               bool& live) {
-    const uint32_t ui = idx >= 0 ? (uint32_t)idx : 0u;
-    const uint32_t blk = fdiv(ui, p.fd_bs);
-    const uint32_t off = ui - blk * p.fd_bs.d;
-    int64_t page;
-    if constexpr (TABLE) {
-        const bool inb = idx >= 0 && blk < (uint32_t)p.max_blocks;
-        page = (inb && word >= 0 && word < p.num_blocks) ? (int64_t)word : -1;
-    } else {
-        page = (idx >= 0 && blk < p.num_blocks) ? (int64_t)blk : -1;
-    }
-    live = page >= 0;
-    const uint8_t* base = p.kv + (live ? page : 0) * p.page_stride;
-    const int64_t z = reinterpret_cast<int64_t>(kZeroRow);
-    const int64_t d = reinterpret_cast<int64_t>(base + off * kRowData);
-    const int64_t s = reinterpret_cast<int64_t>(base + p.fd_bs.d * kRowData + off * kRowScale);
-    return PatchSrc{(gbyte*)(live ? d : z), (gbyte*)(live ? s : z + kRowData)};
-}
-
-// Reductions over groups of N consecutive lanes (N = 8 or 16) of a DPP row.
-template <int N>
-__device__ __forceinline__ float group_max(float v) {
-    v = fmaxf(v, dpp<0xB1>(v));
-    v = fmaxf(v, dpp<0x4E>(v));
-    v = fmaxf(v, dpp<0x141>(v));
-    if constexpr (N == 16) v = fmaxf(v, dpp<0x140>(v));
-    return v;
-}
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-    v += dpp<0xB1>(v);
-    v += dpp<0x4E>(v);
-    v += dpp<0x141>(v);
-    if constexpr (N == 16) v += dpp<0x140>(v);
-    return v;
-}
-
-// Position of entry e (0..63, a multiple of 4) of a super-tile in the MFMA
-// k order of PV: within each 32-entry k-step, k = 8g + 4h + i holds entry
-// 16h + 4g + i, the order in which the LDS transpose read delivers V.
-__device__ __forceinline__ int k_slot(int e) {
-    return (e & 32) + 8 * ((e >> 2) & 3) + 4 * ((e >> 4) & 1);
-}
-
-// Dequantised row chunks of one lane into the padded K tile.
-template <int O, bool SCRUB>
-__device__ __forceinline__ void store_row(const uint32_t (&rr)[64], int prow, int l8,
-                                          __bf16* Kt) {
-    const uint64_t sw = (uint64_t)rr[O + 19] << 32 | rr[O + 18];
-    __bf16* dst = Kt + prow * kShortLd + 8 * l8;
-#pragma unroll
-    for (int j = 0; j < 7; ++j) {
-        bf16x8 v = dequant8(make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]),
-                            (uint32_t)(sw >> (8 * j)) & 0xFFu);
-        if (SCRUB) {
-            u32x4 w = __builtin_bit_cast(u32x4, v);
-            w = u32x4{scrub_pair(w[0]), scrub_pair(w[1]), scrub_pair(w[2]), scrub_pair(w[3])};
-            v = __builtin_bit_cast(bf16x8, w);
-        }
-        *reinterpret_cast<bf16x8*>(dst + 64 * j) = v;
-    }
-    __bf16* rdst = Kt + prow * kShortLd + kDNope + 4 * l8;
-#pragma unroll
-    for (int j = 7; j < kChunks; ++j) {
-        uint2 raw = make_uint2(rr[O + 2 * j], rr[O + 2 * j + 1]);
-        if (SCRUB) raw = make_uint2(scrub_pair(raw.x), scrub_pair(raw.y));
-        *reinterpret_cast<uint2*>(rdst + 32 * (j - 7)) = raw;
-    }
 }
 
 template <int HG, bool SCRUB, bool TABLE>
