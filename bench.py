@@ -332,6 +332,11 @@ def main() -> int:
                       "frac": bytes_s / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBPS})
         del ws_s, q_s, idx_s, gs, out_s, lse_s
 
+    # Phase timeline of the headline partial kernel (short-split plans only):
+    # the stamped variant on a cold replica, per-phase medians over the
+    # workgroups in shader-clock cycles.
+    timeline = short_timeline(dsv4, desc, plan, q, kv, gslots_all, sink, out, lse, S, R)
+
     # A measured bandwidth reference: a 1 GiB device-to-device copy.
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
@@ -395,6 +400,7 @@ def main() -> int:
         "measured_copy_GBps": copy_GBps,
         "b_sweep": sweep,
         "event_ms_per_step": ev_ms_per_step,
+        "partial_timeline": timeline,
         "writer": {"rows": wn, "block_size": wbs, "sanitize": True, "replicas": wrep,
                    "ms": kt_writer, "algorithmic_bytes": writer_bytes,
                    "GBps": writer_bytes / (kt_writer * 1e-3) / 1e9,
@@ -415,6 +421,34 @@ def main() -> int:
         rec["cpu_baseline"] = cpu_baseline(w, out, lse, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def short_timeline(dsv4, desc, plan, q, kv, slots_all, sink, out, lse, S, R):
+    """Per-phase breakdown of the short-split kernel (include/dsv4_diag.h,
+    dsv4_short_timeline) on the benchmark's inputs: ten launches over cold
+    replicas, stamps of the last; medians over its workgroups."""
+    import torch
+    if plan.partial_kernel != dsv4.DSV4_KERNEL_SHORT:
+        return None
+    stamps = torch.zeros(plan.grid_partial * 10, dtype=torch.int64, device=q.device)
+    for r in range(10):
+        dsv4.dsv4_short_timeline(desc, q, kv, None, slots_all[(R - 1 - r) % R], None, sink, out,
+                                 lse, S, stamps)
+    torch.cuda.synchronize()
+    t = stamps.view(-1, 10).cpu().numpy().astype(np.int64)
+    t = t[t[:, 1] > 0]
+    cyc = t[:, 8] - t[:, 1]
+    real = np.maximum(1, t[:, 9] - t[:, 0])
+    mhz = float(np.median(cyc / real * 100.0))
+    names = ["resolve_and_issue", "dequant_st0", "barrier_wait", "qk", "softmax", "pv_and_rest",
+             "epilogue"]
+    phases = {n: int(np.median(t[:, k + 2] - t[:, k + 1])) for k, n in enumerate(names)}
+    return {"kernel": f"decode_short_kernel<{plan.heads_per_group}, false, false, true> "
+                      "(stamped variant)",
+            "workgroups": int(t.shape[0]), "clock_MHz": mhz,
+            "wg_span_us_median": float(np.median(real)) / 100.0,
+            "wg_start_spread_us": float(t[:, 0].max() - t[:, 0].min()) / 100.0,
+            "phase_cycles_median": phases}
 
 
 def profile_workload(ci: int, steps: int) -> int:

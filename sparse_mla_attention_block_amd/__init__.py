@@ -127,6 +127,8 @@ _lib.dsv4_convert_req_index_to_global.argtypes = [
 _lib.dsv4_convert_req_index_to_global.restype = ctypes.c_int
 _lib.dsv4_gather_floor.argtypes = [_DESC, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
 _lib.dsv4_gather_floor.restype = ctypes.c_int
+_lib.dsv4_short_timeline.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
+_lib.dsv4_short_timeline.restype = ctypes.c_int
 _lib.dsv4_decode_flags_for_cache.argtypes = [ctypes.c_int32] * 4
 _lib.dsv4_decode_flags_for_cache.restype = ctypes.c_uint32
 _lib.dsv4_sparse_decode_dual.argtypes = [_DESC, _P, ctypes.POINTER(dsv4_cache_pool),
@@ -303,6 +305,19 @@ def dsv4_gather_floor(desc, kv_cache: torch.Tensor, block_table: Optional[torch.
     _check(_lib.dsv4_gather_floor(ctypes.byref(desc), _ptr(kv_cache), _ptr(block_table),
                                   _ptr(topk_idx), _ptr(valid_len), num_splits, _ptr(words),
                                   _stream(stream)))
+
+
+def dsv4_short_timeline(desc, q: torch.Tensor, kv_cache: torch.Tensor,
+                        block_table: Optional[torch.Tensor], topk_idx: torch.Tensor,
+                        valid_len: Optional[torch.Tensor], sink: Optional[torch.Tensor],
+                        out: torch.Tensor, lse: Optional[torch.Tensor], num_splits: int,
+                        stamps: torch.Tensor, stream=None) -> None:
+    """Phase timeline of the short-split kernel (include/dsv4_diag.h): the
+    first decode stage with 10 stamps per workgroup written to `stamps`
+    (int64 [plan.grid_partial * 10])."""
+    _check(_lib.dsv4_short_timeline(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                    _ptr(topk_idx), _ptr(valid_len), _ptr(sink), _ptr(out),
+                                    _ptr(lse), num_splits, _ptr(stamps), _stream(stream)))
 
 
 def workspace_split_views(workspace: torch.Tensor, batch: int, num_heads: int,

@@ -255,6 +255,7 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.fd_sq = dsv4::make_fastdiv((uint32_t)p.sq);
     p.fd_bs = dsv4::make_fastdiv((uint32_t)p.bs);
     p.fd_bs2 = p.fd_bs;
+    p.timeline = nullptr;
     return p;
 }
 
@@ -394,6 +395,28 @@ int dsv4_gather_floor(const dsv4_decode_desc* desc, const void* kv_cache,
                                              valid_len, nullptr, nullptr, nullptr);
     (void)hipGetLastError();
     return launched(dsv4::launch_gather_floor(p, plan.grid_partial, words, stream), "gather floor");
+}
+
+int dsv4_short_timeline(const dsv4_decode_desc* desc, const void* q, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* topk_idx,
+                        const int32_t* valid_len, const float* sink, void* out, float* lse,
+                        int32_t num_splits, uint64_t* stamps, hipStream_t stream) {
+    Shape sh;
+    dsv4_plan plan;
+    int st = make_plan(desc, num_splits, &sh, &plan);
+    if (st) return st;
+    if (!sh.short_kernel || (desc->flags & DSV4_DECODE_SCRUB))
+        return fail(DSV4_ERR_NOT_SUPPORTED,
+                    "the timeline covers the short-split kernel without scrub only");
+    if (!stamps) return fail(DSV4_ERR_INVALID_ARGUMENT, "stamps must not be NULL");
+    st = check_decode_ptrs(desc, plan, q, kv_cache, block_table, topk_idx, out);
+    if (st) return st;
+    dsv4::DecodeParams p = make_params(desc, sh, q, kv_cache, block_table, topk_idx, valid_len,
+                                       sink, out, lse);
+    p.timeline = stamps;
+    (void)hipGetLastError();
+    return launched(dsv4::launch_decode_short(p, sh.hg, plan.grid_partial, false, stream),
+                    "decode short (timeline)");
 }
 
 int dsv4_sparse_decode_partial(const dsv4_decode_desc* desc, const void* q,

@@ -63,7 +63,9 @@ size_t short_lds_bytes(int hg) {
     return hg == 16 ? ShortSmem<16>::bytes : hg == 32 ? ShortSmem<32>::bytes : ShortSmem<64>::bytes;
 }
 
-template <int HG, bool SCRUB, bool TABLE>
+// STAMPS: thread 0 of each workgroup records its phase timeline into
+// p.timeline (a measurement variant; see dsv4_short_timeline).
+template <int HG, bool SCRUB, bool TABLE, bool STAMPS = false>
 __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodeParams p) {
     constexpr int MT = HG / 16;
     static_assert(MT == 1 || MT == 2 || MT == 4, "short kernel head groups: 16, 32, 64");
@@ -79,6 +81,15 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
+    // Stamps stay in scalar registers and are stored once, at the end, so
+    // that recording them changes the instruction stream as little as it can.
+    uint64_t ts[kTimelineStamps] = {};
+    auto mark = [&](int k, bool real) __attribute__((always_inline)) {
+        if constexpr (STAMPS)
+            ts[k] = real ? __builtin_amdgcn_s_memrealtime() : __builtin_amdgcn_s_memtime();
+    };
+    mark(0, true);
+    mark(1, false);
 
     // Work unit: the pipelined kernel's mapping (head groups of one split
     // kXcds apart, on one XCD), in 32-bit arithmetic.
@@ -157,8 +168,11 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
         vflag[prow] = live0 ? 1 : 0;
         vflag[kShortRows + prow] = live1 ? 1 : 0;
     }
+    mark(2, false);
     store_row<0, SCRUB>(rr, prow, l8, Kt);
+    mark(3, false);
     __syncthreads();
+    mark(4, false);
 
     // Online-softmax state of a softmax lane's head (replicated over its TPH
     // lanes), base-2 units.
@@ -197,6 +211,7 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
             }
         }
         __syncthreads();
+        if (st == 0) mark(5, false);
 
         // 3. Mask + online softmax of the super-tile.
         if (sm_active) {
@@ -235,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
             if (sm_j == 0) alpha_s[sm_h] = a;
         }
         __syncthreads();
+        if (st == 0) mark(6, false);
 
         // 4. PV: O^T += V^T P^T over the super-tile's k-steps.
 #pragma unroll
@@ -273,6 +289,7 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
         }
     }
 
+    mark(7, false);
     // Epilogue: output scale and lse per head (one softmax lane per head).
     const bool direct = p.S == 1;
     if (sm_active && sm_j == 0) {
@@ -324,12 +341,28 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
             *reinterpret_cast<bf16x4*>(orow + 16 * nt) = o;
         }
     }
+    if constexpr (STAMPS) {
+        mark(8, false);
+        mark(9, true);
+        if (tid == 0) {
+            uint64_t* stamp = p.timeline + (size_t)blockIdx.x * kTimelineStamps;
+#pragma unroll
+            for (int k = 0; k < kTimelineStamps; ++k) stamp[k] = ts[k];
+        }
+    }
 }
 
 template <int HG>
 static void launch_short_hg(const DecodeParams& p, dim3 g, bool scrub, hipStream_t stream) {
     const dim3 blk(kThreads);
     const bool table = p.bt != nullptr;
+    if (p.timeline) {
+        if (table)
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, true, true>), g, blk, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, false, true>), g, blk, 0, stream, p);
+        return;
+    }
     if (scrub) {
         if (table)
             hipLaunchKernelGGL((decode_short_kernel<HG, true, true>), g, blk, 0, stream, p);

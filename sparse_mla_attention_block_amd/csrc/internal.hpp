@@ -99,7 +99,12 @@ struct DecodeParams {
     // Launch-time divisors (the short-split kernel): splits, head groups,
     // tokens per sequence, and the block sizes of the two pools.
     FastDiv fd_S, fd_G, fd_sq, fd_bs, fd_bs2;
+    // Measurement aid (short-split kernel only): per-workgroup phase stamps,
+    // kTimelineStamps words per workgroup, or null.
+    uint64_t* timeline;
 };
+
+constexpr int kTimelineStamps = 10;
 
 struct CombineParams {
     const uint16_t* part_o;     // bf16 [B, H, S, 512]

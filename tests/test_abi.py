@@ -355,3 +355,20 @@ def test_selector_never_asks_for_a_second_round_of_workgroups(H):
             tiles = -(-Kt // 32)
             per = -(-tiles // p.num_splits)
             assert -(-tiles // per) == p.num_splits          # no split without entries
+
+
+def test_short_timeline_refuses_other_kernels_without_touching_the_gpu():
+    """The phase timeline exists for the short-split kernel only: a plan that
+    picks the pipelined kernel (the large batch) or the scrub flag is refused
+    before any pointer is looked at."""
+    import ctypes
+    c = CONFIGS[3]
+    d = _desc(c["B"], c["H"], c["topk"], c["swa"])
+    assert dsv4.dsv4_sparse_decode_plan(d, 0).partial_kernel == dsv4.DSV4_KERNEL_PIPELINED
+    st = dsv4._lib.dsv4_short_timeline(ctypes.byref(d), None, None, None, None, None, None, None,
+                                      None, 0, None, None)
+    assert st == dsv4.DSV4_ERR_NOT_SUPPORTED and "short-split" in dsv4.dsv4_last_error()
+    d = _desc(1, 64, 2048, 0, flags=dsv4.DSV4_DECODE_SCRUB)
+    st = dsv4._lib.dsv4_short_timeline(ctypes.byref(d), None, None, None, None, None, None, None,
+                                      None, 0, None, None)
+    assert st == dsv4.DSV4_ERR_NOT_SUPPORTED
