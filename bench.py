@@ -1,10 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse FP8 MLA decode hot path on one MI355X.
 
-One step = one pass of the whole path over one batch:
-  1. req-local -> global slot conversion through the block table (fill -1),
-  2. the decode partial kernel over the global slots,
-  3. the split combine kernel (when the selector picks S > 1).
+One step = one pass of the whole path over one batch, two launches:
+  1. the partial kernel, which resolves the req-local top-k indices through
+     the block table and also writes their req-local -> global conversion
+     (fill -1) from the same index and table loads;
+  2. the split combine kernel (when the selector picks S > 1).
+That is dsv4_sparse_decode_with_slots.  The sequential form of the same work
+(a conversion launch, then the partial kernel over the global slots, then the
+combine: three launches) is timed beside it.
 The workload is the long-context low-batch decode: B=1 query token, H=64
 heads, top-k 2048 of 131072 cache slots (block size 64, shuffled pages, 1 %
 invalid), fp8_ds_mla rows, sink logits, softmax scale 512^-0.5.
@@ -93,16 +97,16 @@ def _source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic_from_profile(digest: str):
+def _traffic_from_profile(digest: str, kernel: str):
     """HBM bytes per launch of the partial kernel from the committed counter
-    summary, if it was taken on the current kernel source."""
+    summary, if it was taken on the current kernel source and kernel variant."""
     path = os.path.join(ROOT, "profiles", "decode_partial_long_lowbatch_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_digest") != digest:
+    if rec.get("kernel_source_digest") != digest or rec.get("kernel") != kernel:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -158,6 +162,12 @@ def main() -> int:
                           flags=flags)
     part_o, part_l = dsv4.workspace_split_views(ws, B, H, S) if S > 1 else (None, None)
     kv = pool.view(-1)
+    # The block-table form of the same decode (req-local indices).
+    desc_tbl = dsv4.make_desc(batch=B, num_heads=H, topk=w.topk, swa=w.swa,
+                              block_size=w.block_size, num_blocks=R * nb, page_stride=stride,
+                              sm_scale=w.sm_scale, max_blocks_per_seq=maxb,
+                              block_table_stride=maxb, workspace=ws, flags=flags)
+    plan_tbl = dsv4.dsv4_sparse_decode_plan(desc_tbl, S)
 
     def convert(r, dst):
         dsv4.dsv4_convert_req_index_to_global(None, B, bt_all[r * B:(r + 1) * B], maxb, maxb, idx,
@@ -166,11 +176,19 @@ def main() -> int:
     def partial(slots):
         dsv4.dsv4_sparse_decode_partial(desc, q, kv, None, slots, None, sink, out, lse, S)
 
+    def partial_tbl(r):
+        dsv4.dsv4_sparse_decode_partial_with_slots(desc_tbl, q, kv, bt_all[r * B:(r + 1) * B],
+                                                   idx, None, sink, out, lse, S, gslots)
+
     def combine():
         if S > 1:
             dsv4.dsv4_combine_splits(B, H, S, part_o, part_l, sink, out, lse)
 
     def step(r):
+        dsv4.dsv4_sparse_decode_with_slots(desc_tbl, q, kv, bt_all[r * B:(r + 1) * B], idx, None,
+                                           sink, out, lse, S, gslots)
+
+    def step_seq(r):
         convert(r, gslots)
         partial(gslots)
         combine()
@@ -247,16 +265,24 @@ def main() -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    # The conversion's output of the timed steps, checked against a fresh
+    # conversion of the same replica's table.
+    conv_timed = gslots.clone()
+    last_r = (W + K - 1) % R
+    conv_ok = bool(torch.equal(conv_timed, gslots_all[last_r]))
+
     kt_conv = time_graph(capture(lambda r: convert(r, gslots), K), K)
-    kt_part = time_graph(capture(lambda r: partial(gslots_all[r]), K), K)
+    kt_part = time_graph(capture(partial_tbl, K), K)
+    kt_part_slots = time_graph(capture(lambda r: partial(gslots_all[r]), K), K)
     kt_comb = time_graph(capture(lambda r: combine(), K), K) if S > 1 else 0.0
+    seq_ms_per_step = time_graph(capture(step_seq, K), K)
 
     # Floors: the partial kernel's own gather (same grid, same row loads over
     # the same rotating replicas, no arithmetic), and an empty launch (a
     # 4-byte fill kernel) for the launch cost of a graph node.
     words = torch.empty(plan.grid_partial * plan.block_partial, dtype=torch.int32, device=dev)
     kt_gather = time_graph(capture(lambda r: dsv4.dsv4_gather_floor(
-        desc, kv, None, gslots_all[r], None, S, words), K), K)
+        desc_tbl, kv, bt_all[r * B:(r + 1) * B], idx, None, S, words), K), K)
     tiny = torch.empty(1, dtype=torch.int32, device=dev)
     kt_empty = time_graph(capture(lambda r: tiny.fill_(r), K), K)
 
@@ -285,12 +311,15 @@ def main() -> int:
     # Cache-warm reference: one replica, same step.
     g_hot = capture(lambda r: step(0), K)
     hot_ms_per_step = time_graph(g_hot, K)
-    kt_part_hot = time_graph(capture(lambda r: partial(gslots_all[0]), K), K)
+    kt_part_hot = time_graph(capture(lambda r: partial_tbl(0), K), K)
 
-    partial(gslots_all[0])
+    partial_tbl(0)
     combine()
     torch.cuda.synchronize()
     same = bool(torch.equal(out_timed, out) and torch.equal(lse_timed, lse))
+    step_seq(0)
+    torch.cuda.synchronize()
+    same_seq = bool(torch.equal(out_timed, out) and torch.equal(lse_timed, lse))
 
     # B-sweep of the headline shape: B tokens per step with the same index
     # list, token b of a step reading its own cache replica (same rows,
@@ -301,12 +330,12 @@ def main() -> int:
         if 2 * Bs > R:
             break
         dk = dict(batch=Bs, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
-                  num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale)
+                  num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale,
+                  max_blocks_per_seq=maxb, block_table_stride=maxb)
         plan_s = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**dk), 0)
         Ss = plan_s.num_splits
         ws_s = torch.empty(max(plan_s.workspace_bytes, 16), dtype=torch.uint8, device=dev)
         desc_s = dsv4.make_desc(workspace=ws_s, **dk)
-        po_s, pl_s = dsv4.workspace_split_views(ws_s, Bs, H, Ss) if Ss > 1 else (None, None)
         q_s = q.expand(Bs, H, 512).contiguous()
         idx_s = idx.expand(Bs, Kt).contiguous()
         gs = torch.empty((Bs, Kt), dtype=torch.int32, device=dev)
@@ -314,15 +343,11 @@ def main() -> int:
         lse_s = torch.empty((Bs, H), dtype=torch.float32, device=dev)
         nrot = R // Bs
 
-        def step_s(r, Bs=Bs, Ss=Ss, desc_s=desc_s, po_s=po_s, pl_s=pl_s, q_s=q_s, idx_s=idx_s,
-                   gs=gs, out_s=out_s, lse_s=lse_s, nrot=nrot):
+        def step_s(r, Bs=Bs, Ss=Ss, desc_s=desc_s, q_s=q_s, idx_s=idx_s, gs=gs, out_s=out_s,
+                   lse_s=lse_s, nrot=nrot):
             start = (r % nrot) * Bs
-            dsv4.dsv4_convert_req_index_to_global(None, Bs, bt_all[start:start + Bs], maxb, maxb,
-                                                  idx_s, Kt, Bs, Kt, w.block_size, None, -1, gs)
-            dsv4.dsv4_sparse_decode_partial(desc_s, q_s, kv, None, gs, None, sink, out_s, lse_s,
-                                            Ss)
-            if Ss > 1:
-                dsv4.dsv4_combine_splits(Bs, H, Ss, po_s, pl_s, sink, out_s, lse_s)
+            dsv4.dsv4_sparse_decode_with_slots(desc_s, q_s, kv, bt_all[start:start + Bs], idx_s,
+                                               None, sink, out_s, lse_s, Ss, gs)
 
         ms_s = time_graph(capture(step_s, K2), K2)
         bytes_s = Bs * (n_valid_slots * (ROW_BYTES + INDEX_BYTES) + H * 512 * 2 * 2)
@@ -335,7 +360,8 @@ def main() -> int:
     # Phase timeline of the headline partial kernel (short-split plans only):
     # the stamped variant on a cold replica, per-phase medians over the
     # workgroups in shader-clock cycles.
-    timeline = short_timeline(dsv4, desc, plan, q, kv, gslots_all, sink, out, lse, S, R)
+    timeline = short_timeline(dsv4, desc_tbl, plan_tbl, q, kv, bt_all, B, idx, sink, out, lse, S,
+                              R)
 
     # A measured bandwidth reference: a 1 GiB device-to-device copy.
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -354,7 +380,12 @@ def main() -> int:
     tokens_per_s = n_valid / (ms_per_step * 1e-3)
     achieved = part_bytes / (kt_part * 1e-3) / 1e9
     digest = _source_digest()
-    traffic = None if args.scrub else _traffic_from_profile(digest)
+    kname = (("decode_short_kernel" if plan_tbl.partial_kernel == dsv4.DSV4_KERNEL_SHORT
+              else "decode_partial_kernel")
+             + f"<{plan_tbl.heads_per_group}, {'true' if args.scrub else 'false'}"
+             + (", true, false, true>" if plan_tbl.partial_kernel == dsv4.DSV4_KERNEL_SHORT
+                else ">"))
+    traffic = None if args.scrub else _traffic_from_profile(digest, kname)
 
     rec = {
         "metric": METRIC,
@@ -377,14 +408,13 @@ def main() -> int:
             "heads_per_group": plan.heads_per_group, "scrub": bool(args.scrub),
             "replicas": R, "cache_pool_GB": round(R * nb * stride / 1e9, 2),
             "graph_replay": not args.eager, "parallelism": "single GPU",
+            "step": "partial kernel resolving the indices through the block table and "
+                    "writing their global slots, then the combine",
         },
         "achieved_hbm_GBps_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("decode_short_kernel" if plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT
-                       else "decode_partial_kernel")
-                      + f"<{plan.heads_per_group}, {'true' if args.scrub else 'false'}"
-                      + (", false>" if plan.partial_kernel else ">"),
+            "kernel": kname,
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -394,7 +424,8 @@ def main() -> int:
             "algorithmic_bytes_per_launch": part_bytes,
             "mfma_frac": flops / (kt_part * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         },
-        "kernels_ms": {"convert": kt_conv, "decode_partial": kt_part, "combine": kt_comb},
+        "kernels_ms": {"convert": kt_conv, "decode_partial": kt_part, "combine": kt_comb,
+                       "decode_partial_global_slots": kt_part_slots},
         "floors_ms": {"gather_only": kt_gather, "empty_launch": kt_empty,
                       "partial_over_gather": kt_part / kt_gather},
         "measured_copy_GBps": copy_GBps,
@@ -408,6 +439,16 @@ def main() -> int:
         "cache_warm": {"ms_per_step": hot_ms_per_step, "decode_partial_ms": kt_part_hot,
                        "tokens_per_s": n_valid / (hot_ms_per_step * 1e-3)},
         "timed_output_matches_single_call": same,
+        "launches_per_step": 2 if S > 1 else 1,
+        "conversion_output_matches": conv_ok,
+        "sequential_step": {
+            "steps": "conversion, then the partial kernel over the global slots, then the "
+                     "combine, in one stream",
+            "launches_per_step": 3 if S > 1 else 2,
+            "ms_per_step": seq_ms_per_step,
+            "tokens_per_s": n_valid / (seq_ms_per_step * 1e-3),
+            "output_matches_step": same_seq,
+        },
         "kernel_source_digest": digest,
     }
 
@@ -423,16 +464,18 @@ def main() -> int:
     return 0
 
 
-def short_timeline(dsv4, desc, plan, q, kv, slots_all, sink, out, lse, S, R):
+def short_timeline(dsv4, desc, plan, q, kv, bt_all, B, idx, sink, out, lse, S, R):
     """Per-phase breakdown of the short-split kernel (include/dsv4_diag.h,
-    dsv4_short_timeline) on the benchmark's inputs: ten launches over cold
-    replicas, stamps of the last; medians over its workgroups."""
+    dsv4_short_timeline) on the benchmark's inputs (block-table form): ten
+    launches over cold replicas, stamps of the last; medians over its
+    workgroups."""
     import torch
     if plan.partial_kernel != dsv4.DSV4_KERNEL_SHORT:
         return None
     stamps = torch.zeros(plan.grid_partial * 10, dtype=torch.int64, device=q.device)
-    for r in range(10):
-        dsv4.dsv4_short_timeline(desc, q, kv, None, slots_all[(R - 1 - r) % R], None, sink, out,
+    for i in range(10):
+        r = (R - 1 - i) % R
+        dsv4.dsv4_short_timeline(desc, q, kv, bt_all[r * B:(r + 1) * B], idx, None, sink, out,
                                  lse, S, stamps)
     torch.cuda.synchronize()
     t = stamps.view(-1, 10).cpu().numpy().astype(np.int64)
@@ -443,7 +486,7 @@ def short_timeline(dsv4, desc, plan, q, kv, slots_all, sink, out, lse, S, R):
     names = ["resolve_and_issue", "dequant_st0", "barrier_wait", "qk", "softmax", "pv_and_rest",
              "epilogue"]
     phases = {n: int(np.median(t[:, k + 2] - t[:, k + 1])) for k, n in enumerate(names)}
-    return {"kernel": f"decode_short_kernel<{plan.heads_per_group}, false, false, true> "
+    return {"kernel": f"decode_short_kernel<{plan.heads_per_group}, false, true, true> "
                       "(stamped variant)",
             "workgroups": int(t.shape[0]), "clock_MHz": mhz,
             "wg_span_us_median": float(np.median(real)) / 100.0,

@@ -217,6 +217,45 @@ int dsv4_sparse_decode(const dsv4_decode_desc* desc, const void* q, const void* 
                        const int32_t* valid_len, const float* sink, void* out, float* lse,
                        int32_t num_splits, hipStream_t stream);
 
+/* dsv4_sparse_decode through a block table that also writes the req-local
+ * -> global conversion of the same indices, so that a decode step which
+ * needs both the attention output and the global slots (later consumers of
+ * the slots) reads the indices and the table once.
+ * (vLLM PR #52212 page, implementation item 1: the decode resolves entries
+ * through the block table; vLLM PR #41217 report, key source snippets: the
+ * req-index to global-index conversion.)
+ *   block_table   required (int32 [B / s_q, block_table_stride])
+ *   global_slots  int32 [B, topk + swa], contiguous, 4-byte aligned, device:
+ *                 exactly what dsv4_convert_req_index_to_global writes for
+ *                 topk_idx with req_id[t] = t / s_q, num_reqs = B / s_q,
+ *                 width = topk + swa, ti_stride = topk_idx_stride,
+ *                 max_blocks_per_req = desc->max_blocks_per_seq, no
+ *                 cu_seqlens and invalid_fill = -1.  Every column is
+ *                 converted, the masked tail [valid_len, topk) included.
+ * out and lse are the bytes dsv4_sparse_decode writes for the same
+ * arguments.  When the plan picks the short-split kernel
+ * (dsv4_plan.partial_kernel) that kernel writes the slots from the index
+ * and table loads it makes anyway; otherwise a conversion launch precedes
+ * the decode on the same stream.  Errors as dsv4_sparse_decode, plus
+ * INVALID_ARGUMENT for a NULL block_table or global_slots or a misaligned
+ * global_slots (nothing launched). */
+int dsv4_sparse_decode_with_slots(const dsv4_decode_desc* desc, const void* q,
+                                  const void* kv_cache, const int32_t* block_table,
+                                  const int32_t* topk_idx, const int32_t* valid_len,
+                                  const float* sink, void* out, float* lse, int32_t num_splits,
+                                  int32_t* global_slots, hipStream_t stream);
+
+/* First stage of dsv4_sparse_decode_with_slots alone: the split partials (or,
+ * with S = 1, out and lse) exactly as dsv4_sparse_decode_partial writes
+ * them, and the global slots exactly as dsv4_sparse_decode_with_slots
+ * writes them.  Same arguments and errors as dsv4_sparse_decode_with_slots. */
+int dsv4_sparse_decode_partial_with_slots(const dsv4_decode_desc* desc, const void* q,
+                                          const void* kv_cache, const int32_t* block_table,
+                                          const int32_t* topk_idx, const int32_t* valid_len,
+                                          const float* sink, void* out, float* lse,
+                                          int32_t num_splits, int32_t* global_slots,
+                                          hipStream_t stream);
+
 /* First stage of dsv4_sparse_decode alone.  With S = 1 it writes out/lse
  * directly (the same bytes dsv4_sparse_decode writes).  With S > 1 it
  * writes, for every (b, h, split), the split's normalised partial output

@@ -128,6 +128,11 @@ _lib.dsv4_convert_req_index_to_global.restype = ctypes.c_int
 _lib.dsv4_gather_floor.argtypes = [_DESC, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
 _lib.dsv4_gather_floor.restype = ctypes.c_int
 _lib.dsv4_short_timeline.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P]
+_lib.dsv4_sparse_decode_with_slots.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               ctypes.c_int32, _P, _P]
+_lib.dsv4_sparse_decode_with_slots.restype = ctypes.c_int
+_lib.dsv4_sparse_decode_partial_with_slots.argtypes = _lib.dsv4_sparse_decode_with_slots.argtypes
+_lib.dsv4_sparse_decode_partial_with_slots.restype = ctypes.c_int
 _lib.dsv4_short_timeline.restype = ctypes.c_int
 _lib.dsv4_decode_flags_for_cache.argtypes = [ctypes.c_int32] * 4
 _lib.dsv4_decode_flags_for_cache.restype = ctypes.c_uint32
@@ -225,6 +230,34 @@ def dsv4_sparse_decode_noalloc(desc: dsv4_decode_desc, q: torch.Tensor, kv_cache
                                            _ptr(block_table), _ptr(topk_idx), _ptr(valid_len),
                                            _ptr(sink), _ptr(out), _ptr(lse), num_splits,
                                            _stream(stream)))
+
+
+def dsv4_sparse_decode_with_slots(desc: dsv4_decode_desc, q: torch.Tensor,
+                                  kv_cache: torch.Tensor, block_table: torch.Tensor,
+                                  topk_idx: torch.Tensor, valid_len: Optional[torch.Tensor],
+                                  sink: Optional[torch.Tensor], out: torch.Tensor,
+                                  lse: Optional[torch.Tensor], num_splits: int,
+                                  global_slots: torch.Tensor, stream=None) -> None:
+    """dsv4_sparse_decode through the block table that also writes the global
+    slots of topk_idx (int32 [B, topk + swa], fill -1) into `global_slots`."""
+    _check(_lib.dsv4_sparse_decode_with_slots(ctypes.byref(desc), _ptr(q), _ptr(kv_cache),
+                                              _ptr(block_table), _ptr(topk_idx), _ptr(valid_len),
+                                              _ptr(sink), _ptr(out), _ptr(lse), num_splits,
+                                              _ptr(global_slots), _stream(stream)))
+
+
+def dsv4_sparse_decode_partial_with_slots(desc: dsv4_decode_desc, q: torch.Tensor,
+                                          kv_cache: torch.Tensor, block_table: torch.Tensor,
+                                          topk_idx: torch.Tensor,
+                                          valid_len: Optional[torch.Tensor],
+                                          sink: Optional[torch.Tensor], out: torch.Tensor,
+                                          lse: Optional[torch.Tensor], num_splits: int,
+                                          global_slots: torch.Tensor, stream=None) -> None:
+    """First stage of dsv4_sparse_decode_with_slots alone."""
+    _check(_lib.dsv4_sparse_decode_partial_with_slots(
+        ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(topk_idx),
+        _ptr(valid_len), _ptr(sink), _ptr(out), _ptr(lse), num_splits, _ptr(global_slots),
+        _stream(stream)))
 
 
 def dsv4_sparse_decode_partial(desc: dsv4_decode_desc, q: torch.Tensor, kv_cache: torch.Tensor,

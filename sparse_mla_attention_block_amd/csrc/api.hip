@@ -256,6 +256,7 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.fd_bs = dsv4::make_fastdiv((uint32_t)p.bs);
     p.fd_bs2 = p.fd_bs;
     p.timeline = nullptr;
+    p.slots = nullptr;
     return p;
 }
 
@@ -284,10 +285,13 @@ int check_pool(const dsv4_cache_pool* pl, const char* which) {
     return DSV4_OK;
 }
 
+// slots (single pool with a block table only): also write the req-local ->
+// global conversion of every index column, inside the short-split kernel
+// when the plan picks it, else with a conversion launch before the decode.
 int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const int32_t* bt,
                 const int32_t* idx, const int32_t* valid_len, const float* sink, void* out,
                 float* lse, int32_t num_splits, hipStream_t stream, bool with_combine,
-                const dsv4_cache_pool* swa_pool = nullptr) {
+                const dsv4_cache_pool* swa_pool = nullptr, int32_t* slots = nullptr) {
     Shape sh;
     dsv4_plan plan;
     int st = make_plan(d, num_splits, &sh, &plan);
@@ -306,6 +310,31 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
         p.max_blocks2 = swa_pool->block_table ? swa_pool->max_blocks_per_seq : 0;
     }
     (void)hipGetLastError();   // start from a clean error state
+    if (slots) {
+        if (sh.short_kernel) {
+            p.slots = slots;
+        } else {
+            if (sh.kt > 65535 * 256)
+                return fail(DSV4_ERR_INVALID_ARGUMENT, "topk + swa too large for the conversion");
+            dsv4::ConvertParams c;
+            c.req_id = nullptr;
+            c.bt = bt;
+            c.ti = idx;
+            c.cu = nullptr;
+            c.out = slots;
+            c.bt_stride = d->block_table_stride;
+            c.ti_stride = sh.idx_stride;
+            c.num_reqs = d->batch / p.sq;
+            c.max_blocks = d->max_blocks_per_seq;
+            c.num_tokens = d->batch;
+            c.width = (int32_t)sh.kt;
+            c.bs = d->block_size;
+            c.fill = -1;
+            c.sq = p.sq;
+            st = launched(dsv4::launch_convert(c, stream), "convert");
+            if (st) return st;
+        }
+    }
     const bool scrub = (d->flags & DSV4_DECODE_SCRUB) != 0;
     st = sh.short_kernel && !swa_pool
              ? launched(dsv4::launch_decode_short(p, sh.hg, plan.grid_partial, scrub, stream),
@@ -323,6 +352,19 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
     c.H = d->num_heads;
     c.S = sh.splits;
     return launched(dsv4::launch_combine(c, stream), "combine");
+}
+
+int decode_with_slots(const dsv4_decode_desc* desc, const void* q, const void* kv_cache,
+                      const int32_t* block_table, const int32_t* topk_idx,
+                      const int32_t* valid_len, const float* sink, void* out, float* lse,
+                      int32_t num_splits, int32_t* global_slots, hipStream_t stream,
+                      bool with_combine) {
+    if (!block_table || !global_slots)
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "block_table and global_slots must not be NULL");
+    if (!aligned(global_slots, 4))
+        return fail(DSV4_ERR_INVALID_ARGUMENT, "global_slots must be 4-byte aligned");
+    return decode_impl(desc, q, kv_cache, block_table, topk_idx, valid_len, sink, out, lse,
+                       num_splits, stream, with_combine, nullptr, global_slots);
 }
 
 }  // namespace
@@ -373,6 +415,25 @@ int dsv4_sparse_decode(const dsv4_decode_desc* desc, const void* q, const void* 
                        int32_t num_splits, hipStream_t stream) {
     return decode_impl(desc, q, kv_cache, block_table, topk_idx, valid_len, sink, out, lse,
                        num_splits, stream, true);
+}
+
+int dsv4_sparse_decode_with_slots(const dsv4_decode_desc* desc, const void* q,
+                                  const void* kv_cache, const int32_t* block_table,
+                                  const int32_t* topk_idx, const int32_t* valid_len,
+                                  const float* sink, void* out, float* lse, int32_t num_splits,
+                                  int32_t* global_slots, hipStream_t stream) {
+    return decode_with_slots(desc, q, kv_cache, block_table, topk_idx, valid_len, sink, out, lse,
+                             num_splits, global_slots, stream, true);
+}
+
+int dsv4_sparse_decode_partial_with_slots(const dsv4_decode_desc* desc, const void* q,
+                                          const void* kv_cache, const int32_t* block_table,
+                                          const int32_t* topk_idx, const int32_t* valid_len,
+                                          const float* sink, void* out, float* lse,
+                                          int32_t num_splits, int32_t* global_slots,
+                                          hipStream_t stream) {
+    return decode_with_slots(desc, q, kv_cache, block_table, topk_idx, valid_len, sink, out, lse,
+                             num_splits, global_slots, stream, false);
 }
 
 int dsv4_gather_floor(const dsv4_decode_desc* desc, const void* kv_cache,
@@ -485,6 +546,7 @@ int dsv4_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
     p.width = width;
     p.bs = block_size;
     p.fill = invalid_fill;
+    p.sq = 1;
     (void)hipGetLastError();
     return launched(dsv4::launch_convert(p, stream), "convert");
 }

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kConvertThreads) void convert_kernel(const ConvertP
     if (i >= n) return;
     // Positions outside [0, cu[num_tokens]) are never written, whatever cu holds.
     if (p.cu && (base + i < 0 || base + i >= p.cu[p.num_tokens])) return;
-    const int32_t req = p.req_id ? p.req_id[t] : t;
+    const int32_t req = p.req_id ? p.req_id[t] : p.sq == 1 ? t : t / p.sq;
     const int32_t idx = p.ti[(int64_t)t * p.ti_stride + i];
     int64_t v = p.fill;
     if (idx >= 0 && req >= 0 && req < p.num_reqs) {

@@ -65,10 +65,16 @@ size_t short_lds_bytes(int hg) {
 
 // STAMPS: thread 0 of each workgroup records its phase timeline into
 // p.timeline (a measurement variant; see dsv4_short_timeline).
-template <int HG, bool SCRUB, bool TABLE, bool STAMPS = false>
+// EMIT (with TABLE): the workgroups of head group 0 also write the req-local
+// -> global conversion of the token's index row into p.slots (vLLM PR #41217
+// report, key source snippets: the conversion kernel), split s taking
+// columns [s*cc, s*cc + cc) with cc = ceil((topk + swa) / S) <= 128, one per
+// lane; its index and table loads ride in the decode's own round trips.
+template <int HG, bool SCRUB, bool TABLE, bool STAMPS = false, bool EMIT = false>
 __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodeParams p) {
     constexpr int MT = HG / 16;
     static_assert(MT == 1 || MT == 2 || MT == 4, "short kernel head groups: 16, 32, 64");
+    static_assert(!EMIT || (TABLE && !STAMPS), "the conversion output needs the block table");
     using L = ShortSmem<HG>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::bytes];
     __bf16* Kt = reinterpret_cast<__bf16*>(smem + L::kn);
@@ -125,6 +131,18 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
     };
     const int32_t i0 = index_at(e0);
     const int32_t i1 = index_at(e1);
+    // Conversion column of this lane (EMIT).
+    const uint32_t kt = (uint32_t)(p.topk + p.swa);
+    int cv_col = 0;
+    bool cv_on = false;
+    int32_t cv_idx = -1;
+    if constexpr (EMIT) {
+        const uint32_t cc = fdiv(kt + (uint32_t)p.S - 1, p.fd_S);
+        cv_col = (int)(s * cc) + tid;
+        cv_on = g == 0 && tid < (int)cc && (uint32_t)cv_col < kt;
+        const int32_t v = *global(irow + (cv_on ? cv_col : 0));
+        cv_idx = cv_on ? v : -1;
+    }
 
     // QK assignment: 16 heads cut the dot into two k halves (wave w: row
     // block w&3, half w>>2); 32 heads give each wave one (row block, head
@@ -160,6 +178,8 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
     // split's end), all unconditional.
     const int32_t w0 = table_word<TABLE>(p, seq, i0);
     const int32_t w1 = table_word<TABLE>(p, seq, i1);
+    int32_t cv_word = 0;
+    if constexpr (EMIT) cv_word = table_word<true>(p, seq, cv_idx);
     uint32_t rr[64];
     bool live0, live1;
     load_patch<0>(row_source<TABLE>(p, i0, w0, live0), l8, rr);
@@ -171,6 +191,18 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
     mark(2, false);
     store_row<0, SCRUB>(rr, prow, l8, Kt);
     mark(3, false);
+    if constexpr (EMIT) {
+        // The conversion's rule: a negative index, a block past the table, a
+        // negative page entry or a slot past INT32_MAX give the fill -1.
+        if (cv_on) {
+            const uint32_t ui = cv_idx >= 0 ? (uint32_t)cv_idx : 0u;
+            const uint32_t blk = fdiv(ui, p.fd_bs);
+            const int64_t gs = (int64_t)cv_word * p.fd_bs.d + (ui - blk * p.fd_bs.d);
+            const bool ok = cv_idx >= 0 && blk < (uint32_t)p.max_blocks && cv_word >= 0 &&
+                            gs <= (int64_t)INT32_MAX;
+            p.slots[(int64_t)b * kt + cv_col] = ok ? (int32_t)gs : -1;
+        }
+    }
     __syncthreads();
     mark(4, false);
 
@@ -363,6 +395,15 @@ static void launch_short_hg(const DecodeParams& p, dim3 g, bool scrub, hipStream
             hipLaunchKernelGGL((decode_short_kernel<HG, false, false, true>), g, blk, 0, stream, p);
         return;
     }
+    if (p.slots) {
+        if (scrub)
+            hipLaunchKernelGGL((decode_short_kernel<HG, true, true, false, true>), g, blk, 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, true, false, true>), g, blk, 0,
+                               stream, p);
+        return;
+    }
     if (scrub) {
         if (table)
             hipLaunchKernelGGL((decode_short_kernel<HG, true, true>), g, blk, 0, stream, p);
@@ -379,6 +420,8 @@ static void launch_short_hg(const DecodeParams& p, dim3 g, bool scrub, hipStream
 hipError_t launch_decode_short(const DecodeParams& p, int heads_per_group, int64_t grid,
                                bool scrub, hipStream_t stream) {
     if (p.kv2 != nullptr) return hipErrorInvalidValue;     // single pool only
+    if (p.slots != nullptr && (p.bt == nullptr || p.timeline != nullptr))
+        return hipErrorInvalidValue;
     const dim3 g((unsigned)grid);
     switch (heads_per_group) {
         case 16: launch_short_hg<16>(p, g, scrub, stream); break;

@@ -102,6 +102,10 @@ struct DecodeParams {
     // Measurement aid (short-split kernel only): per-workgroup phase stamps,
     // kTimelineStamps words per workgroup, or null.
     uint64_t* timeline;
+    // Short-split kernel with a block table only: the req-local -> global
+    // conversion of every index column, int32 [B, topk + swa], fill -1; or
+    // null.
+    int32_t* slots;
 };
 
 constexpr int kTimelineStamps = 10;
@@ -124,6 +128,7 @@ struct ConvertParams {
     int64_t bt_stride;
     int64_t ti_stride;
     int32_t num_reqs, max_blocks, num_tokens, width, bs, fill;
+    int32_t sq;                 // without req_id: token t reads table row t / sq
 };
 
 struct StoreParams {

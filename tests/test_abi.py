@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
                  "dsv4_convert_req_index_to_global", "dsv4_sparse_decode_plan",
                  "dsv4_sparse_decode_workspace_bytes", "dsv4_status_string", "dsv4_last_error",
                  "dsv4_gather_floor", "dsv4_quantize_store", "dsv4_gather_dequant",
-                 "dsv4_dense_decode", "dsv4_decode_flags_for_cache", "dsv4_sparse_decode_dual"):
+                 "dsv4_dense_decode", "dsv4_decode_flags_for_cache", "dsv4_sparse_decode_dual",
+                 "dsv4_sparse_decode_with_slots"):
         assert want in names
 
 
@@ -260,6 +261,24 @@ def test_decode_rejects_null_and_missing_workspace_without_touching_the_gpu():
     assert dsv4._lib.dsv4_combine_splits(1, 64, 0, fake, fake, None, fake, None, None) == \
         dsv4.DSV4_ERR_INVALID_ARGUMENT
     assert dsv4.dsv4_status_string(3) == "DSV4_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_decode_with_slots_validation_without_touching_the_gpu():
+    d = _desc(1, 64, 100, 0)
+    d.max_blocks_per_seq, d.block_table_stride = 2, 2
+    fake = ctypes.c_void_p(4096)
+    f = dsv4._lib.dsv4_sparse_decode_with_slots
+    # no block table, no slots buffer, a misaligned slots buffer
+    assert f(ctypes.byref(d), fake, fake, None, fake, None, None, fake, None, 1, fake,
+             None) == dsv4.DSV4_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, None, 1, None,
+             None) == dsv4.DSV4_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, None, 1,
+             ctypes.c_void_p(4098), None) == dsv4.DSV4_ERR_INVALID_ARGUMENT
+    assert "global_slots" in dsv4.dsv4_last_error()
+    # the decode's own checks still apply (split partials need a workspace)
+    assert f(ctypes.byref(d), fake, fake, fake, fake, None, None, fake, None, 4, fake,
+             None) == dsv4.DSV4_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_writer_validation_without_touching_the_gpu():
