@@ -115,11 +115,14 @@ static void decode_ok(const DecodeParams& p, int hg, int64_t grid) {
     need(p.S == 1 || (p.part_o && p.part_lse), "split workspace");
 }
 hipError_t launch_decode_partial(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
-    decode_ok(p, hg, grid); ++g_launches; return hipSuccess;
+    decode_ok(p, hg, grid);
+    need(p.slots == nullptr, "slots reach only the short-split kernel");
+    ++g_launches; return hipSuccess;
 }
 hipError_t launch_decode_short(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
     decode_ok(p, hg, grid);
     need(hg == 16 || hg == 32 || hg == 64, "short-kernel head group");
+    need(p.slots == nullptr || p.bt != nullptr, "slots need the block table");
     ++g_launches; return hipSuccess;
 }
 size_t short_lds_bytes(int) { return 0; }
@@ -187,6 +190,26 @@ int main(void) {
                                      DEV(0x6000), (float*)DEV(0x7000), S, NULL) == DSV4_OK);
             n += plan.num_splits > 1 ? 2 : 1;
             CHECK(stub_launches() == n);
+            /* The slot-writing decode: one launch more (the conversion) unless the
+               short-split kernel writes the slots itself. */
+            CHECK(dsv4_sparse_decode_with_slots(&d, DEV(0x1000), DEV(0x2000),
+                                                (const int32_t*)DEV(0x3000),
+                                                (const int32_t*)DEV(0x4000), NULL, NULL,
+                                                DEV(0x6000), NULL, S, (int32_t*)DEV(0x8000),
+                                                NULL) == DSV4_OK);
+            n += (plan.num_splits > 1 ? 2 : 1) + (plan.partial_kernel == DSV4_KERNEL_SHORT ? 0 : 1);
+            CHECK(stub_launches() == n);
+            CHECK(dsv4_sparse_decode_partial_with_slots(&d, DEV(0x1000), DEV(0x2000),
+                                                        (const int32_t*)DEV(0x3000),
+                                                        (const int32_t*)DEV(0x4000), NULL, NULL,
+                                                        DEV(0x6000), NULL, S,
+                                                        (int32_t*)DEV(0x8000), NULL) == DSV4_OK);
+            n += plan.partial_kernel == DSV4_KERNEL_SHORT ? 1 : 2;
+            CHECK(stub_launches() == n);
+            CHECK(dsv4_sparse_decode_with_slots(&d, DEV(0x1000), DEV(0x2000), NULL,
+                                                (const int32_t*)DEV(0x4000), NULL, NULL,
+                                                DEV(0x6000), NULL, S, (int32_t*)DEV(0x8000),
+                                                NULL) == DSV4_ERR_INVALID_ARGUMENT);
             if (ws) {
                 d.workspace_bytes = ws - 1;
                 CHECK(dsv4_sparse_decode(&d, DEV(0x1000), DEV(0x2000), NULL,
