@@ -590,10 +590,9 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
         desc_pipe = dsv4.make_desc(workspace=ws, flags=dsv4.DSV4_DECODE_PIPELINED, **kw)
         kv = pool.view(-1)
 
-        def timed(rot, d=desc):
+        def timed(rot, d=desc, S=w.num_splits):
             def decode(r):
-                dsv4.dsv4_sparse_decode(d, q, kv, bts[r], idx, vl, sink, out, lse,
-                                        w.num_splits)
+                dsv4.dsv4_sparse_decode(d, q, kv, bts[r], idx, vl, sink, out, lse, S)
 
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
@@ -619,6 +618,16 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
         kname = "short" if plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT else "pipelined"
         pipe = {"pipelined_warm_us": timed(False, desc_pipe),
                 "pipelined_cold_us": timed(True, desc_pipe)} if kname != "pipelined" else {}
+        # The short-context batch's configured plan (split-K capped at 4, the
+        # pages' short-list cap) beside the selector's.
+        cap4 = {}
+        if w.name == "short_batch":
+            plan4 = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**kw), 4)
+            cap4 = {"cap4_plan": {
+                "num_splits": plan4.num_splits, "heads_per_group": plan4.heads_per_group,
+                "partial_kernel": ("short" if plan4.partial_kernel == dsv4.DSV4_KERNEL_SHORT
+                                   else "pipelined"),
+                "warm_us": timed(False, desc, 4), "cold_us": timed(True, desc, 4)}}
         nbytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * (512 * 2 * 2 + 4)
         flops = n_valid * 2048 * H
         gbps = nbytes / (cold_us * 1e-6) / 1e9
@@ -627,7 +636,7 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
             "workload": w.name, "B": B, "H": H, "topk": w.topk, "swa": w.swa,
             "valid_entries": n_valid, "heads_per_group": plan.heads_per_group,
             "num_splits": plan.num_splits, "grid_partial": plan.grid_partial,
-            "partial_kernel": kname, **pipe,
+            "partial_kernel": kname, **pipe, **cap4,
             "replicas": R, "MB_between_reuse": round(R * touched / 1e6, 1),
             "warm_us": warm_us, "cold_us": cold_us,
             "tokens_per_s": n_valid / (cold_us * 1e-6),
