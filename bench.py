@@ -68,8 +68,8 @@ def _parse():
                          "(0-4) --steps times, for counter passes, and print its algorithmic "
                          "work as JSON")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the batch sweep (profiler runs: its launches share the headline "
-                         "kernel's name)")
+                    help="skip the batch and split-count sweeps (profiler runs: their launches "
+                         "share the headline kernel's name)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the per-workload decode table (all five seeded workloads)")
     ap.add_argument("--no-context-parallel", action="store_true",
@@ -357,6 +357,27 @@ def main() -> int:
                       "frac": bytes_s / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBPS})
         del ws_s, q_s, idx_s, gs, out_s, lse_s
 
+    # The headline step at forced split counts (the selector picks 32).
+    split_sweep = []
+    for Sf in () if args.no_sweep else (8, 16, 32, 64):
+        dk = dict(batch=B, num_heads=H, topk=w.topk, swa=w.swa, block_size=w.block_size,
+                  num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale,
+                  max_blocks_per_seq=maxb, block_table_stride=maxb, flags=flags)
+        plan_f = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**dk), Sf)
+        ws_f = torch.empty(max(plan_f.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+        desc_f = dsv4.make_desc(workspace=ws_f, **dk)
+
+        def step_f(r, Sf=Sf, desc_f=desc_f):
+            dsv4.dsv4_sparse_decode_with_slots(desc_f, q, kv, bt_all[r * B:(r + 1) * B], idx, None,
+                                               sink, out, lse, Sf, gslots)
+
+        ms_f = time_graph(capture(step_f, K2), K2)
+        split_sweep.append({"num_splits": Sf, "heads_per_group": plan_f.heads_per_group,
+                            "partial_kernel": ("short" if plan_f.partial_kernel ==
+                                               dsv4.DSV4_KERNEL_SHORT else "pipelined"),
+                            "ms_per_step": ms_f, "tokens_per_s": n_valid_slots / (ms_f * 1e-3)})
+        del ws_f
+
     # Phase timeline of the headline partial kernel (short-split plans only):
     # the stamped variant on a cold replica, per-phase medians over the
     # workgroups in shader-clock cycles.
@@ -430,6 +451,7 @@ def main() -> int:
                       "partial_over_gather": kt_part / kt_gather},
         "measured_copy_GBps": copy_GBps,
         "b_sweep": sweep,
+        "split_sweep": split_sweep,
         "event_ms_per_step": ev_ms_per_step,
         "partial_timeline": timeline,
         "writer": {"rows": wn, "block_size": wbs, "sanitize": True, "replicas": wrep,
