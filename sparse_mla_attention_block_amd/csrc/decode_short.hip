@@ -94,6 +94,16 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
         if constexpr (STAMPS)
             ts[k] = real ? __builtin_amdgcn_s_memrealtime() : __builtin_amdgcn_s_memtime();
     };
+    // Every kernel argument the kernel reads, in one batch of scalar loads
+    // and one wait: otherwise the compiler loads them in three batches, each
+    // after a branch that depends on the one before.
+    asm volatile("" ::"s"(p.q), "s"(p.kv), "s"(p.bt), "s"(p.idx), "s"(p.valid_len),
+                 "s"(p.sink), "s"(p.out), "s"(p.lse), "s"(p.part_o), "s"(p.part_lse),
+                 "s"(p.num_blocks), "s"(p.bt_stride), "s"(p.page_stride), "s"(p.idx_stride),
+                 "s"(p.units), "s"(p.H), "s"(p.topk), "s"(p.swa), "s"(p.max_blocks), "s"(p.S),
+                 "s"(p.G), "s"(p.qk_scale_log2), "s"(p.slots), "s"(p.timeline));
+    asm volatile("" ::"s"(p.fd_S.d), "s"(p.fd_S.m), "s"(p.fd_S.l), "s"(p.fd_G.m), "s"(p.fd_G.l),
+                 "s"(p.fd_sq.m), "s"(p.fd_sq.l), "s"(p.fd_bs.d), "s"(p.fd_bs.m), "s"(p.fd_bs.l));
     mark(0, true);
     mark(1, false);
 
