@@ -115,10 +115,14 @@ def test_masked_tail_and_head_groups(H, S):
 
 
 @pytest.mark.parametrize("s_q,S", [(2, 3), (3, 4)])
-def test_multi_token_rows_read_their_sequence(s_q, S):
+@pytest.mark.parametrize("kernel", [1, 0])
+def test_multi_token_rows_read_their_sequence(s_q, S, kernel):
+    """Token t reads table row t // s_q, in the short-split kernel's own
+    conversion and in the conversion launch before the pipelined kernel."""
     w = make_custom(B=3, H=64, topk=256, swa=64, seq_lens=[4000, 700, 300], seed=410 + s_q,
                     invalid_frac=0.03, valid_len_range=(100, 256), s_q=s_q)
-    _check(w, S, f"s_q={s_q}", expect_kernel=dsv4.DSV4_KERNEL_SHORT)
+    flags = 0 if kernel == dsv4.DSV4_KERNEL_SHORT else dsv4.DSV4_DECODE_PIPELINED
+    _check(w, S, f"s_q={s_q} kernel={kernel}", expect_kernel=kernel, flags=flags)
 
 
 @pytest.mark.parametrize("S,kernel", [(4, 1), (1, 1), (4, 0)])
