@@ -233,9 +233,10 @@ int dsv4_sparse_decode(const dsv4_decode_desc* desc, const void* q, const void* 
  *                 cu_seqlens and invalid_fill = -1.  Every column is
  *                 converted, the masked tail [valid_len, topk) included.
  * out and lse are the bytes dsv4_sparse_decode writes for the same
- * arguments.  When the plan picks the short-split kernel
- * (dsv4_plan.partial_kernel) that kernel writes the slots from the index
- * and table loads it makes anyway; otherwise a conversion launch precedes
+ * arguments.  The partial kernel writes the slots from index and table
+ * loads issued beside its own: the short-split kernel always, the
+ * pipelined kernel when a split covers at most 1024 index columns
+ * (ceil((topk + swa) / S) <= 1024); otherwise a conversion launch precedes
  * the decode on the same stream.  Errors as dsv4_sparse_decode, plus
  * INVALID_ARGUMENT for a NULL block_table or global_slots or a misaligned
  * global_slots (nothing launched). */

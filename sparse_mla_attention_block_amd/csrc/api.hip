@@ -311,7 +311,10 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
     }
     (void)hipGetLastError();   // start from a clean error state
     if (slots) {
-        if (sh.short_kernel) {
+        // Inside the partial kernel when it can (the short-split kernel always;
+        // the pipelined one with at most 1024 index columns per split), else a
+        // conversion launch first.
+        if (sh.short_kernel || ceil_div(sh.kt, sh.splits) <= 2 * dsv4::kThreads) {
             p.slots = slots;
         } else {
             if (sh.kt > 65535 * 256)

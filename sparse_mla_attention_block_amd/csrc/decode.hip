@@ -52,8 +52,14 @@ namespace dsv4 {
 // The partial kernel's body.  SCRUB: non-finite dequantised elements read
 // as 0.  DENSE: rows come from a gathered bf16 buffer [B, idx_stride, 512]
 // with a per-entry mask (1 = takes no part) instead of the FP8 cache.
-template <int HG, bool SCRUB, bool DENSE>
+// EMIT (block table, single pool): the workgroups of head group 0 also write
+// the req-local -> global conversion of the token's index row into p.slots
+// (vLLM PR #41217 report, key source snippets: the conversion kernel), split
+// s taking columns [s*cc, s*cc + cc), cc = ceil((topk + swa) / S) <= 1024,
+// two per thread, with loads issued beside the resolution's own.
+template <int HG, bool SCRUB, bool DENSE, bool EMIT = false>
 __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
+    static_assert(!(EMIT && DENSE), "the conversion output needs the FP8 cache's table");
     constexpr int MT = HG / 16;              // 16-head MFMA tiles; consumer wave w owns tile w
     static_assert(HG % 16 == 0 && HG <= kMaxHeadsPerGroup, "head group");
     using L = Smem<HG>;
@@ -125,10 +131,43 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         } else {
             const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
             const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
+            // Conversion columns of this thread (EMIT), loaded unconditionally.
+            const int kt = p.topk + p.swa;
+            int col0 = 0, col1 = 0;
+            bool on0 = false, on1 = false;
+            int32_t ci0 = -1, ci1 = -1;
+            if constexpr (EMIT) {
+                const int cc = (kt + p.S - 1) / p.S;
+                col0 = s * cc + tid;
+                col1 = col0 + kThreads;
+                on0 = g == 0 && tid < cc && col0 < kt;
+                on1 = g == 0 && tid + kThreads < cc && col1 < kt;
+                const int32_t* row = p.idx + (int64_t)b * p.idx_stride;
+                const int32_t v0 = row[on0 ? col0 : 0];
+                const int32_t v1 = row[on1 ? col1 : 0];
+                ci0 = on0 ? v0 : -1;
+                ci1 = on1 ? v1 : -1;
+            }
             const Pool pl0 = pool_of(p, lo + tid >= vl);
             const Pool pl1 = pool_of(p, lo + kThreads + tid >= vl);
             const int64_t g0 = lookup_page(p, pl0, seq, i0);
             const int64_t g1 = lookup_page(p, pl1, seq, i1);
+            if constexpr (EMIT) {
+                // The conversion's rule: a negative index, a block past the
+                // table, a negative page entry or a slot past INT32_MAX give -1.
+                auto emit = [&](int32_t ci, int col, bool on) __attribute__((always_inline)) {
+                    const bool ok = ci >= 0;
+                    const int64_t blk = (ok ? ci : 0) / p.bs;
+                    const bool inb = ok && blk < p.max_blocks;
+                    const int32_t w = p.bt[(int64_t)seq * p.bt_stride + (inb ? blk : 0)];
+                    const int64_t gs = (int64_t)w * p.bs + (ok ? ci : 0) % p.bs;
+                    if (on)
+                        p.slots[(int64_t)b * kt + col] =
+                            inb && w >= 0 && gs <= (int64_t)INT32_MAX ? (int32_t)gs : -1;
+                };
+                emit(ci0, col0, on0);
+                emit(ci1, col1, on1);
+            }
             write_meta(pl0, meta + 2 * tid, g0, i0);
             write_meta(pl1, meta + 2 * (kThreads + tid), g1, i1);
             b0 = __builtin_amdgcn_ballot_w64(g0 >= 0);
@@ -548,9 +587,9 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     }
 }
 
-template <int HG, bool SCRUB>
+template <int HG, bool SCRUB, bool EMIT = false>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
-    decode_partial_body<HG, SCRUB, false>(p);
+    decode_partial_body<HG, SCRUB, false, EMIT>(p);
 }
 
 // Attention over gathered bf16 rows (second kernel of the two-kernel path).
@@ -833,6 +872,16 @@ template <bool SCRUB>
 static hipError_t launch_partial_variant(const DecodeParams& p, int heads_per_group,
                                          dim3 g, hipStream_t stream) {
     const dim3 blk(kThreads);
+    if (p.slots) {
+        switch (heads_per_group) {
+            case 16: hipLaunchKernelGGL((decode_partial_kernel<16, SCRUB, true>), g, blk, 0, stream, p); break;
+            case 32: hipLaunchKernelGGL((decode_partial_kernel<32, SCRUB, true>), g, blk, 0, stream, p); break;
+            case 48: hipLaunchKernelGGL((decode_partial_kernel<48, SCRUB, true>), g, blk, 0, stream, p); break;
+            case 64: hipLaunchKernelGGL((decode_partial_kernel<64, SCRUB, true>), g, blk, 0, stream, p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (heads_per_group) {
         case 16: hipLaunchKernelGGL((decode_partial_kernel<16, SCRUB>), g, blk, 0, stream, p); break;
         case 32: hipLaunchKernelGGL((decode_partial_kernel<32, SCRUB>), g, blk, 0, stream, p); break;
@@ -870,6 +919,11 @@ hipError_t launch_gather_dequant(const DecodeParams& p, uint16_t* kv_out, uint8_
 
 hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int64_t grid,
                                  bool scrub, hipStream_t stream) {
+    // The conversion output needs the block table, a single pool and at most
+    // 1024 columns per split.
+    if (p.slots != nullptr &&
+        (p.bt == nullptr || p.kv2 != nullptr || (p.topk + p.swa + p.S - 1) / p.S > 2 * kThreads))
+        return hipErrorInvalidValue;
     const dim3 g((unsigned)grid);
     return scrub ? launch_partial_variant<true>(p, heads_per_group, g, stream)
                  : launch_partial_variant<false>(p, heads_per_group, g, stream);

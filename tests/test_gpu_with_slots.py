@@ -4,8 +4,9 @@ The slots are checked bit for bit against the oracle's conversion of the same
 index rows (req_id[t] = t // s_q, fill -1, every column including the masked
 tail), and out/lse bit for bit against dsv4_sparse_decode with the same
 arguments (the same arithmetic, in a kernel that also writes the slots).
-Both paths of the entry point run: the conversion inside the short-split
-kernel, and a conversion launch before the pipelined kernel.
+All paths of the entry point run: the conversion inside the short-split
+kernel, inside the pipelined kernel (at most 1024 index columns a split), and
+a conversion launch before the pipelined kernel (more columns a split).
 """
 
 import dataclasses
@@ -86,11 +87,21 @@ def _check(w, S, what, idx_pad=0, expect_kernel=None, flags=0):
 
 @pytest.mark.parametrize("ci,kernel", [(0, 1), (1, 1), (2, 1), (3, 0), (4, 0)])
 def test_workloads_at_the_selector_plan(ci, kernel):
-    """All five workloads: short-split kernel (conversion inside it) for the
-    first three, pipelined kernel with a conversion launch for the large
-    batch and the ragged batch (whose masked tails are converted too)."""
+    """All five workloads: the short-split kernel for the first three, the
+    pipelined kernel for the large batch and the ragged batch (whose masked
+    tails are converted too), each writing the slots itself."""
     w = make_workload(ci)
     _check(w, w.num_splits, w.name, expect_kernel=kernel)
+
+
+@pytest.mark.parametrize("ci,S", [(2, 1), (4, 2)])
+def test_conversion_launch_when_a_split_has_over_1024_columns(ci, S):
+    """The pipelined kernel writes the slots itself for at most 1024 index
+    columns a split; past that (one split over 2048 columns, two over 2176)
+    a conversion launch precedes the decode."""
+    w = make_workload(ci)
+    assert (w.Kt + S - 1) // S > 1024
+    _check(w, S, f"{w.name} S={S} (conversion launch)", expect_kernel=dsv4.DSV4_KERNEL_PIPELINED)
 
 
 @pytest.mark.parametrize("ci,S", [(1, 8), (1, 5), (2, 16), (2, 64), (0, 1)])

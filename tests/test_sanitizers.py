@@ -116,7 +116,8 @@ static void decode_ok(const DecodeParams& p, int hg, int64_t grid) {
 }
 hipError_t launch_decode_partial(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
     decode_ok(p, hg, grid);
-    need(p.slots == nullptr, "slots reach only the short-split kernel");
+    need(p.slots == nullptr || (p.bt != nullptr && (p.topk + p.swa + p.S - 1) / p.S <= 1024),
+         "slots need the block table and at most 1024 columns per split");
     ++g_launches; return hipSuccess;
 }
 hipError_t launch_decode_short(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
@@ -190,21 +191,28 @@ int main(void) {
                                      DEV(0x6000), (float*)DEV(0x7000), S, NULL) == DSV4_OK);
             n += plan.num_splits > 1 ? 2 : 1;
             CHECK(stub_launches() == n);
-            /* The slot-writing decode: one launch more (the conversion) unless the
-               short-split kernel writes the slots itself. */
+            /* The slot-writing decode: one launch more (the conversion) only when
+               the pipelined kernel would have more than 1024 index columns a split. */
             CHECK(dsv4_sparse_decode_with_slots(&d, DEV(0x1000), DEV(0x2000),
                                                 (const int32_t*)DEV(0x3000),
                                                 (const int32_t*)DEV(0x4000), NULL, NULL,
                                                 DEV(0x6000), NULL, S, (int32_t*)DEV(0x8000),
                                                 NULL) == DSV4_OK);
-            n += (plan.num_splits > 1 ? 2 : 1) + (plan.partial_kernel == DSV4_KERNEL_SHORT ? 0 : 1);
-            CHECK(stub_launches() == n);
+            {
+                const int kt = shapes[i][2] + shapes[i][3];
+                const int conv = plan.partial_kernel != DSV4_KERNEL_SHORT &&
+                                 (kt + plan.num_splits - 1) / plan.num_splits > 1024;
+                n += (plan.num_splits > 1 ? 2 : 1) + conv;
+                CHECK(stub_launches() == n);
+            }
             CHECK(dsv4_sparse_decode_partial_with_slots(&d, DEV(0x1000), DEV(0x2000),
                                                         (const int32_t*)DEV(0x3000),
                                                         (const int32_t*)DEV(0x4000), NULL, NULL,
                                                         DEV(0x6000), NULL, S,
                                                         (int32_t*)DEV(0x8000), NULL) == DSV4_OK);
-            n += plan.partial_kernel == DSV4_KERNEL_SHORT ? 1 : 2;
+            n += (plan.partial_kernel != DSV4_KERNEL_SHORT &&
+                  (shapes[i][2] + shapes[i][3] + plan.num_splits - 1) / plan.num_splits > 1024)
+                     ? 2 : 1;
             CHECK(stub_launches() == n);
             CHECK(dsv4_sparse_decode_with_slots(&d, DEV(0x1000), DEV(0x2000), NULL,
                                                 (const int32_t*)DEV(0x4000), NULL, NULL,
