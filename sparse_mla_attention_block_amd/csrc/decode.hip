@@ -115,10 +115,27 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     uint32_t rr[64];
     float sink_l2 = -INFINITY;                   // consumer lane's sink, base-2 units
 
+    // q row of the consumer lane's head into rr (see above).
+    auto load_q = [&]() __attribute__((always_inline)) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(
+            p.q + ((int64_t)b * p.H + h0 + hc) * kD + 8 * lg);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const u32x4 v = qp[4 * ks];
+            rr[4 * ks] = v[0];
+            rr[4 * ks + 1] = v[1];
+            rr[4 * ks + 2] = v[2];
+            rr[4 * ks + 3] = v[3];
+        }
+    };
+
     // Resolution of the first 32 tiles (the whole ring): two entries per
     // thread, then a per-tile bit mask of the rows that take part (wave w
     // covers tiles 2w, 2w+1 and 16+2w, 17+2w).  Later tiles are resolved 16 at
     // a time inside the loop, which only splits longer than 32 tiles reach.
+    // Consumer waves issue their q loads right after the block-table loads,
+    // so q streams in during the table round trip (issued before the index
+    // loads it would hold them back: loads retire in order).
     {
         uint64_t b0, b1;
         if constexpr (DENSE) {
@@ -129,9 +146,8 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             b0 = __builtin_amdgcn_ballot_w64(v0);
             b1 = __builtin_amdgcn_ballot_w64(v1);
         } else {
-            const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
-            const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
-            // Conversion columns of this thread (EMIT), loaded unconditionally.
+            // Conversion columns of this thread (EMIT), loaded unconditionally
+            // and before the ring entries, so both sets arrive in one round trip.
             const int kt = p.topk + p.swa;
             int col0 = 0, col1 = 0;
             bool on0 = false, on1 = false;
@@ -148,25 +164,41 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
                 ci0 = on0 ? v0 : -1;
                 ci1 = on1 ? v1 : -1;
             }
+            const int32_t i0 = load_index(p, b, vl, hi, lo + tid);
+            const int32_t i1 = load_index(p, b, vl, hi, lo + kThreads + tid);
             const Pool pl0 = pool_of(p, lo + tid >= vl);
             const Pool pl1 = pool_of(p, lo + kThreads + tid >= vl);
-            const int64_t g0 = lookup_page(p, pl0, seq, i0);
-            const int64_t g1 = lookup_page(p, pl1, seq, i1);
+            // All table loads of the block (ring entries and conversion
+            // columns) are issued before any is used: one round trip.  The
+            // slot-writing variant always has a table.
+            int32_t w0 = 0, w1 = 0, cw0 = 0, cw1 = 0;
+            if (EMIT || p.bt) {
+                w0 = pl0.bt[(int64_t)seq * pl0.bt_stride + table_column(pl0, i0)];
+                w1 = pl1.bt[(int64_t)seq * pl1.bt_stride + table_column(pl1, i1)];
+                if constexpr (EMIT) {
+                    const Pool pm = pool_of(p, false);
+                    cw0 = p.bt[(int64_t)seq * p.bt_stride + table_column(pm, ci0)];
+                    cw1 = p.bt[(int64_t)seq * p.bt_stride + table_column(pm, ci1)];
+                }
+            }
+            if (consumer) load_q();
+            const int64_t g0 = page_from_word(p, pl0, i0, w0);
+            const int64_t g1 = page_from_word(p, pl1, i1, w1);
             if constexpr (EMIT) {
                 // The conversion's rule: a negative index, a block past the
                 // table, a negative page entry or a slot past INT32_MAX give -1.
-                auto emit = [&](int32_t ci, int col, bool on) __attribute__((always_inline)) {
+                auto emit = [&](int32_t ci, int32_t w, int col, bool on)
+                                __attribute__((always_inline)) {
                     const bool ok = ci >= 0;
                     const int64_t blk = (ok ? ci : 0) / p.bs;
                     const bool inb = ok && blk < p.max_blocks;
-                    const int32_t w = p.bt[(int64_t)seq * p.bt_stride + (inb ? blk : 0)];
                     const int64_t gs = (int64_t)w * p.bs + (ok ? ci : 0) % p.bs;
                     if (on)
                         p.slots[(int64_t)b * kt + col] =
                             inb && w >= 0 && gs <= (int64_t)INT32_MAX ? (int32_t)gs : -1;
                 };
-                emit(ci0, col0, on0);
-                emit(ci1, col1, on1);
+                emit(ci0, cw0, col0, on0);
+                emit(ci1, cw1, col1, on1);
             }
             write_meta(pl0, meta + 2 * tid, g0, i0);
             write_meta(pl1, meta + 2 * (kThreads + tid), g1, i1);
@@ -182,21 +214,13 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     }
     __syncthreads();
 
-    // q is loaded only now, beside the producers' first row loads: issued
-    // before the index loads it would hold them back (loads retire in order).
-    if (consumer) {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(
-            p.q + ((int64_t)b * p.H + h0 + hc) * kD + 8 * lg);
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const u32x4 v = qp[4 * ks];
-            rr[4 * ks] = v[0];
-            rr[4 * ks + 1] = v[1];
-            rr[4 * ks + 2] = v[2];
-            rr[4 * ks + 3] = v[3];
-        }
-        if (p.sink) sink_l2 = p.sink[h0 + hc] * kLog2e;
+    // Dense rows: q is loaded beside the producers' first row loads.  The
+    // sink (used at the finish) is loaded here, after the resolution: a load
+    // under a branch makes the compiler wait for every older load at the join.
+    if constexpr (DENSE) {
+        if (consumer) load_q();
     }
+    if (consumer && p.sink) sink_l2 = p.sink[h0 + hc] * kLog2e;
 
     if (producer) {
         if constexpr (DENSE) {
@@ -242,16 +266,6 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         const int col = cpos < vl ? cpos : p.topk + (cpos - vl);
         return p.idx[(int64_t)b * p.idx_stride + (pos < hi ? col : 0)];
     };
-    auto bt_col = [&](const Pool& pl, int32_t idx) {
-        const int64_t blk = idx / pl.bs;
-        return idx >= 0 && blk < pl.max_blocks ? blk : (int64_t)0;
-    };
-    auto page_of = [&](const Pool& pl, int32_t idx, int32_t raw) -> int64_t {
-        if (idx < 0) return -1;
-        const int64_t blk = idx / pl.bs;
-        if (p.bt) return blk < pl.max_blocks && raw >= 0 && raw < pl.num_blocks ? raw : -1;
-        return blk < pl.num_blocks ? blk : -1;
-    };
     auto resolve_stage = [&](int t) __attribute__((always_inline)) {
         const int ph = t % kHalfTiles;
         const int nxt = t - ph + kHalfTiles;      // first tile of the next half
@@ -286,12 +300,12 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             r_i1 = e0 + 64 < hi ? r_i1 : -1;
             if (p.bt) {
                 const Pool pl0 = pool_of(p, e0 >= vl), pl1 = pool_of(p, e0 + 64 >= vl);
-                r_p0 = pl0.bt[(int64_t)seq * pl0.bt_stride + bt_col(pl0, r_i0)];
-                r_p1 = pl1.bt[(int64_t)seq * pl1.bt_stride + bt_col(pl1, r_i1)];
+                r_p0 = pl0.bt[(int64_t)seq * pl0.bt_stride + table_column(pl0, r_i0)];
+                r_p1 = pl1.bt[(int64_t)seq * pl1.bt_stride + table_column(pl1, r_i1)];
             }
         } else {
             const Pool pl0 = pool_of(p, e0 >= vl), pl1 = pool_of(p, e0 + 64 >= vl);
-            const int64_t pg0 = page_of(pl0, r_i0, r_p0), pg1 = page_of(pl1, r_i1, r_p1);
+            const int64_t pg0 = page_from_word(p, pl0, r_i0, r_p0), pg1 = page_from_word(p, pl1, r_i1, r_p1);
             int64_t* m = meta_tile(nxt) + 2 * (128 * wave + lane);
             write_meta(pl0, m, pg0, r_i0);
             write_meta(pl1, m + 2 * 64, pg1, r_i1);
@@ -561,8 +575,13 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         }
     }
 
-    // Output: 8-byte stores straight from the accumulators (the final bf16
-    // output, or the split's bf16 partial); 4 lanes cover 32 contiguous bytes.
+    // Output (the final bf16 output, or the split's bf16 partial): the
+    // scaled accumulators are staged as bf16 rows in LDS, where the K buffers
+    // are free after the last step, then written with 16-byte nontemporal
+    // stores, one contiguous 1 KB head row per wave instruction.  Written
+    // straight from the accumulator layout, each store instruction would
+    // scatter 32-byte pieces over 16 rows, and the rows would sit dirty in L2
+    // until the end-of-kernel writeback.
     uint16_t* dst;
     int64_t row_stride;
     if (direct) {
@@ -572,10 +591,14 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         dst = p.part_o + (((int64_t)b * p.H + h0) * p.S + s) * kD;
         row_stride = (int64_t)p.S * kD;
     }
+    constexpr int kOLd = kD + 8;                 // padded staged row (bf16 elements)
+    static_assert(HG * kOLd * 2 <= kKBufs * L::kn_buf, "output staging fits the K buffers");
+    static_assert(HG * 64 % kThreads == 0, "whole 16-byte chunks per thread");
+    __bf16* Ob = Kn;                             // [HG][kOLd]
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const float sc = fin[16 * mt + l16];
-        uint16_t* row = dst + (16 * mt + l16) * row_stride + 64 * wave + 4 * lg;
+        __bf16* row = Ob + (16 * mt + l16) * kOLd + 64 * wave + 4 * lg;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -584,6 +607,15 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             for (int r = 0; r < 4; ++r) o[r] = (__bf16)(acc[mt][nt][r] * sc);
             *reinterpret_cast<bf16x4*>(row + 16 * nt) = o;
         }
+    }
+    __syncthreads();
+    // 16-byte chunk c of the HG x 1 KB block: head row c / 64, chunk c % 64.
+#pragma unroll
+    for (int k = 0; k < HG * 64 / kThreads; ++k) {
+        const int c = tid + k * kThreads;
+        const int h = c >> 6, ch = c & 63;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Ob + h * kOLd + 8 * ch);
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + h * row_stride + 8 * ch));
     }
 }
 
@@ -827,14 +859,24 @@ __global__ __launch_bounds__(kThreads) void gather_floor_kernel(const DecodePara
     constexpr int kRing = kMetaTiles * kTile;            // 1024 entries
     uint32_t acc = 0;
     for (int base = lo; base < hi; base += kRing) {
+        // Two entries a thread: both index loads, then both table loads, in
+        // flight together (two round trips, as in the partial kernel).
+        int32_t id[2], w[2] = {0, 0};
+        Pool pl[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int i = tid + e * kThreads;
-            const int32_t id = load_index(p, b, vl, hi, base + i);
-            const Pool pl = pool_of(p, base + i >= vl);
-            const int64_t pg = lookup_page(p, pl, seq, id);
-            write_meta(pl, addr[i], pg, id);
+            id[e] = load_index(p, b, vl, hi, base + tid + e * kThreads);
+            pl[e] = pool_of(p, base + tid + e * kThreads >= vl);
         }
+        if (p.bt) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                w[e] = pl[e].bt[(int64_t)seq * pl[e].bt_stride + table_column(pl[e], id[e])];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            write_meta(pl[e], addr[tid + e * kThreads], page_from_word(p, pl[e], id[e], w[e]),
+                       id[e]);
         __syncthreads();
         const int n = min(hi - base, kRing);
         for (int r0 = 0; r0 < n; r0 += 4 * 64) {

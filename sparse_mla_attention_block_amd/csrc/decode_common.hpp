@@ -266,6 +266,23 @@ __device__ __forceinline__ int64_t lookup_page(const DecodeParams& p, const Pool
     return (ok && blk < pl.num_blocks) ? blk : -1;
 }
 
+// lookup_page cut in two, for resolving several entries a thread with all
+// their table loads in flight together: the table column to load (0 for an
+// entry that takes no part), then the page from the loaded word (-1: takes
+// no part; without a table the block number is the page).
+__device__ __forceinline__ int64_t table_column(const Pool& pl, int32_t idx) {
+    const int64_t blk = idx / pl.bs;
+    return idx >= 0 && blk < pl.max_blocks ? blk : (int64_t)0;
+}
+
+__device__ __forceinline__ int64_t page_from_word(const DecodeParams& p, const Pool& pl,
+                                                  int32_t idx, int32_t raw) {
+    if (idx < 0) return -1;
+    const int64_t blk = idx / pl.bs;
+    if (p.bt) return blk < pl.max_blocks && raw >= 0 && raw < pl.num_blocks ? raw : -1;
+    return blk < pl.num_blocks ? blk : -1;
+}
+
 // Data and scale-word addresses of the row at (page, idx % bs); the zero row
 // for a row that takes no part.
 __device__ __forceinline__ void write_meta(const Pool& pl, int64_t* row, int64_t page,

@@ -369,11 +369,15 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
         dst = p.part_o + (((int64_t)b * p.H + h0) * p.S + s) * kD;
         row_stride = (int64_t)p.S * kD;
     }
-    uint16_t* obase = dst + l16 * row_stride + 64 * wave + 4 * lg;
+    // The scaled accumulators are staged as bf16 rows in the (now free) K
+    // tile, then written with 16-byte nontemporal stores, one contiguous 1 KB
+    // head row per wave instruction.
+    static_assert(HG <= kShortRows && HG * 64 % kThreads == 0, "output staging");
+    __bf16* obase = Kt + l16 * kShortLd + 64 * wave + 4 * lg;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const float sc = fin[16 * mt + l16];
-        uint16_t* orow = obase + 16 * mt * row_stride;
+        __bf16* orow = obase + 16 * mt * kShortLd;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -382,6 +386,14 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
             for (int r = 0; r < 4; ++r) o[r] = (__bf16)(acc[mt][nt][r] * sc);
             *reinterpret_cast<bf16x4*>(orow + 16 * nt) = o;
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < HG * 64 / kThreads; ++k) {
+        const int c = tid + k * kThreads;
+        const int h = c >> 6, ch = c & 63;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Kt + h * kShortLd + 8 * ch);
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + h * row_stride + 8 * ch));
     }
     if constexpr (STAMPS) {
         mark(8, false);
