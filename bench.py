@@ -652,13 +652,31 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
                 "warm_us": timed(False, desc, 4), "cold_us": timed(True, desc, 4)}}
         nbytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * (512 * 2 * 2 + 4)
         flops = n_valid * 2048 * H
+        # Tokens of different lengths: the same decode with balanced splits
+        # (DSV4_DECODE_BALANCE), split counts following each token's length.
+        bal = {}
+        if w.valid_len is not None:
+            kwb = dict(kw, flags=dsv4.DSV4_DECODE_BALANCE)
+            planb = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**kwb), w.num_splits)
+            if planb.balanced_splits:
+                wsb = torch.empty(planb.workspace_bytes, dtype=torch.uint8, device=dev)
+                descb = dsv4.make_desc(workspace=wsb, **kwb)
+                bw, bc = timed(False, descb), timed(True, descb)
+                bal = {"balanced_plan": {
+                    "split_budget": planb.balanced_splits, "split_slots": planb.num_splits,
+                    "warm_us": bw, "cold_us": bc,
+                    "GBps": nbytes / (bc * 1e-6) / 1e9,
+                    "frac_hbm": nbytes / (bc * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                    "TFLOPs": flops / (bc * 1e-6) / 1e12,
+                    "frac_mfma": flops / (bc * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}}
+                del wsb
         gbps = nbytes / (cold_us * 1e-6) / 1e9
         tflops = flops / (cold_us * 1e-6) / 1e12
         res.append({
             "workload": w.name, "B": B, "H": H, "topk": w.topk, "swa": w.swa,
             "valid_entries": n_valid, "heads_per_group": plan.heads_per_group,
             "num_splits": plan.num_splits, "grid_partial": plan.grid_partial,
-            "partial_kernel": kname, **pipe, **cap4,
+            "partial_kernel": kname, **pipe, **cap4, **bal,
             "replicas": R, "MB_between_reuse": round(R * touched / 1e6, 1),
             "warm_us": warm_us, "cold_us": cold_us,
             "tokens_per_s": n_valid / (cold_us * 1e-6),

@@ -89,6 +89,24 @@ const char* dsv4_last_error(void);
  * differ only by rounding.  For comparing the two kernels. */
 #define DSV4_DECODE_PIPELINED 0x2u
 
+/* DSV4_DECODE_BALANCE: spread the splits over the tokens by their lengths,
+ * for batches whose valid_len differ from token to token.  The plan keeps
+ * its B * S split workgroups per head group (S forced or chosen as usual);
+ * the kernel reads valid_len at run time and gives token b
+ *   n_b = max(1, ceil(eff_b / (32 T))) splits,  eff_b = valid_len[b] + swa,
+ * with T the fewest 32-entry tiles per split for which sum_b n_b <= B * S and
+ * every n_b fits the row's split slots; each token's effective list is cut
+ * into n_b contiguous chunks of whole tiles as usual.  The partials then hold
+ * S' = min(64, S + ceil(S / 4)) split slots per (token, head) row
+ * (plan.num_splits = S', plan.balanced_splits = S); slots a token leaves
+ * unused hold lse = -inf.  It applies to plans that run the pipelined kernel
+ * with S >= 2 and batch <= 64 (plan.balanced_splits != 0 then) and is
+ * ignored otherwise; the global slots of dsv4_sparse_decode_with_slots then
+ * come from a conversion launch, and dsv4_gather_floor and dsv4_dense_decode
+ * reject it.  (vLLM PR #52212 page, implementation item 2: a fixed grid whose
+ * rows take their active splits at run time.) */
+#define DSV4_DECODE_BALANCE 0x4u
+
 /* Provenance gate: the decode flags a cache of this provenance needs.
  * Returns 0 (the scrub may be skipped) only when every condition holds:
  * the cache is in the fp8_ds_mla format, no KV transfer (another engine,
@@ -123,7 +141,8 @@ typedef struct dsv4_decode_desc {
 
 /* What a decode call will launch.  Filled on the host; needs no GPU. */
 typedef struct dsv4_plan {
-    int32_t num_splits;          /* S used (forced, or chosen by the selector)       */
+    int32_t num_splits;          /* S used (forced, or chosen by the selector); split
+                                    slots per row of the partials (see balanced_splits) */
     int32_t heads_per_group;     /* heads one workgroup serves                       */
     int32_t head_groups;         /* H / heads_per_group                              */
     int32_t tile_entries;        /* cache rows per pipeline tile                     */
@@ -134,6 +153,9 @@ typedef struct dsv4_plan {
     size_t workspace_bytes;      /* scratch the call needs (0 if S == 1)             */
     size_t lds_bytes;            /* LDS per partial workgroup                        */
     int32_t partial_kernel;      /* DSV4_KERNEL_PIPELINED or DSV4_KERNEL_SHORT       */
+    int32_t balanced_splits;     /* DSV4_DECODE_BALANCE in effect: the split budget S
+                                    per token (num_splits is then the split slots per
+                                    row, S + ceil(S/4)); 0 = uniform splits          */
 } dsv4_plan;
 
 /* Partial kernels (dsv4_plan.partial_kernel).  The short-split kernel serves

@@ -34,6 +34,7 @@ DSV4_ERR_HIP = 4
 MAX_SPLITS = 64
 DSV4_DECODE_SCRUB = 0x1
 DSV4_DECODE_PIPELINED = 0x2
+DSV4_DECODE_BALANCE = 0x4
 DSV4_KERNEL_PIPELINED = 0
 DSV4_KERNEL_SHORT = 1
 DSV4_STORE_SANITIZE = 0x1
@@ -73,8 +74,11 @@ class dsv4_cache_pool(ctypes.Structure):
 
 def make_pool(kv_cache: torch.Tensor, block_table: Optional[torch.Tensor], *, block_size: int,
               max_blocks_per_seq: int = 0) -> dsv4_cache_pool:
-    """A pool over a [num_blocks, page_stride] uint8 cache tensor."""
+    """A pool over a [num_blocks, page_stride] uint8 cache tensor.  The pool
+    holds references to both tensors, so their memory stays allocated while
+    the pool is in use."""
     pl = dsv4_cache_pool()
+    pl._tensors = (kv_cache, block_table)
     pl.kv_cache = kv_cache.data_ptr()
     pl.block_table = block_table.data_ptr() if block_table is not None else None
     pl.num_blocks, pl.page_stride = kv_cache.shape[0], kv_cache.shape[1]
@@ -97,6 +101,7 @@ class dsv4_plan(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("lds_bytes", ctypes.c_size_t),
         ("partial_kernel", ctypes.c_int32),
+        ("balanced_splits", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

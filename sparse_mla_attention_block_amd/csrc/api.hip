@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "dsv4.h"
@@ -45,7 +46,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Shape {
     int hg;       // heads per workgroup
     int groups;   // head groups
-    int splits;   // S
+    int splits;   // S: split slots per (token, head) row of the partials
+    int bal;      // balanced splits: the split budget per token (units = B * bal); 0 = off
     bool short_kernel;
     int64_t kt;   // topk + swa
     int64_t idx_stride;
@@ -80,7 +82,7 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
         return fail(DSV4_ERR_INVALID_ARGUMENT,
                     "tokens_per_seq must be >= 0 and divide batch (got %d for batch %d)",
                     d->tokens_per_seq, d->batch);
-    const uint32_t known = DSV4_DECODE_SCRUB | DSV4_DECODE_PIPELINED;
+    const uint32_t known = DSV4_DECODE_SCRUB | DSV4_DECODE_PIPELINED | DSV4_DECODE_BALANCE;
     if (d->flags & ~known)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "unknown decode flags 0x%x",
                     (unsigned)(d->flags & ~known));
@@ -158,28 +160,39 @@ int make_plan(const dsv4_decode_desc* d, int32_t num_splits, Shape* sh, dsv4_pla
     const int64_t chunk_max = ceil_div(ceil_div(kt, S), kTile) * kTile;
     const bool short_kernel = chunk_max <= kShortMaxEntries && (hg == 16 || hg == 32 || hg == 64) &&
                               !(d->flags & DSV4_DECODE_PIPELINED);
+    // Balanced splits: the pipelined kernel's plans with S >= 2 and at most
+    // 64 tokens; the partials get S + ceil(S / 4) split slots per row so the
+    // longest tokens can take more than S splits.
+    const int bal = (d->flags & DSV4_DECODE_BALANCE) && !short_kernel && S >= 2 && d->batch <= 64
+                        ? S
+                        : 0;
+    const int slots = bal ? (int)std::min<int64_t>(kMaxSplits, S + ceil_div(S, 4)) : S;
     sh->hg = hg;
     sh->groups = groups;
-    sh->splits = S;
+    sh->splits = slots;
+    sh->bal = bal;
     sh->short_kernel = short_kernel;
     sh->kt = kt;
     sh->idx_stride = idx_stride;
     if (plan) {
         memset(plan, 0, sizeof *plan);
-        plan->num_splits = S;
+        plan->num_splits = slots;
         plan->heads_per_group = hg;
         plan->head_groups = groups;
         plan->tile_entries = kTile;
         plan->grid_partial = grid;
         plan->block_partial = kThreads;
-        const dsv4::CombineShape cs = dsv4::combine_shape((int64_t)d->batch * d->num_heads, S);
-        plan->grid_combine = S > 1 ? cs.grid : 0;
-        plan->block_combine = S > 1 ? cs.block : 0;
+        const dsv4::CombineShape cs =
+            dsv4::combine_shape((int64_t)d->batch * d->num_heads, slots);
+        plan->grid_combine = slots > 1 ? cs.grid : 0;
+        plan->block_combine = slots > 1 ? cs.block : 0;
         plan->workspace_bytes =
-            S > 1 ? (size_t)d->batch * d->num_heads * S * (kD * sizeof(uint16_t) + sizeof(float))
-                  : 0;
+            slots > 1
+                ? (size_t)d->batch * d->num_heads * slots * (kD * sizeof(uint16_t) + sizeof(float))
+                : 0;
         plan->lds_bytes = short_kernel ? short_lds_bytes(hg) : lds_bytes_for(hg);
         plan->partial_kernel = short_kernel ? DSV4_KERNEL_SHORT : DSV4_KERNEL_PIPELINED;
+        plan->balanced_splits = bal;
     }
     return DSV4_OK;
 }
@@ -239,7 +252,7 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.bt_stride = d->block_table_stride;
     p.page_stride = d->page_stride;
     p.idx_stride = sh.idx_stride;
-    p.units = (int64_t)d->batch * sh.splits;
+    p.units = (int64_t)d->batch * (sh.bal ? sh.bal : sh.splits);
     p.B = d->batch;
     p.H = d->num_heads;
     p.topk = d->topk;
@@ -247,6 +260,8 @@ dsv4::DecodeParams make_params(const dsv4_decode_desc* d, const Shape& sh, const
     p.bs = d->block_size;
     p.max_blocks = bt ? d->max_blocks_per_seq : 0;
     p.S = sh.splits;
+    p.bal = sh.bal;
+    p.bal_hi = sh.bal ? (int32_t)ceil_div(ceil_div(sh.kt, sh.bal), dsv4::kTile) : 0;
     p.G = sh.groups;
     p.sq = d->tokens_per_seq > 1 ? d->tokens_per_seq : 1;
     p.qk_scale_log2 = d->sm_scale * 1.4426950408889634f;
@@ -314,7 +329,7 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
         // Inside the partial kernel when it can (the short-split kernel always;
         // the pipelined one with at most 1024 index columns per split), else a
         // conversion launch first.
-        if (sh.short_kernel || ceil_div(sh.kt, sh.splits) <= 2 * dsv4::kThreads) {
+        if (sh.short_kernel || (!sh.bal && ceil_div(sh.kt, sh.splits) <= 2 * dsv4::kThreads)) {
             p.slots = slots;
         } else {
             if (sh.kt > 65535 * 256)
@@ -447,6 +462,9 @@ int dsv4_gather_floor(const dsv4_decode_desc* desc, const void* kv_cache,
     dsv4_plan plan;
     int st = make_plan(desc, num_splits, &sh, &plan);
     if (st) return st;
+    if (sh.bal)
+        return fail(DSV4_ERR_INVALID_ARGUMENT,
+                    "the gather floor takes the uniform split plan (no DSV4_DECODE_BALANCE)");
     if (!kv_cache || !topk_idx || !words)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "kv_cache, topk_idx and words must not be NULL");
     if (block_table) {

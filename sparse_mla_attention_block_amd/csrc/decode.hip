@@ -49,6 +49,82 @@
 
 namespace dsv4 {
 
+// Balanced splits (the batch's tokens in the lanes of one wave, B <= 64):
+// token t has eff_t = valid_len + swa entries and gets n_t = max(1,
+// ceil(eff_t / (32 T))) splits of at most T tiles, with T the fewest tiles
+// for which sum_t n_t stays within the budget B * bal and no n_t exceeds the
+// S split slots (T = ceil(ceil((topk + swa) / bal) / 32) always qualifies).
+// Work unit u is split u - (n_0 + ... + n_{t-1}) of the token t whose range
+// holds it; units past the last token's splits have no work.  Every wave
+// computes the same assignment.  (vLLM PR #52212 page, implementation item
+// 2: a fixed grid whose rows pick their active splits at run time.)
+// ceil(a / d) for 0 <= a < 2^24 and 32 <= d < 2^24: a/d < 2^19, so the
+// quotient from the fp32 reciprocal (relative error below 2^-21) is within
+// one of the exact one, and one integer correction step fixes it.
+__device__ __forceinline__ int ceil_div_small(int a, int d) {
+    int q = (int)((float)a * __builtin_amdgcn_rcpf((float)d));
+    int r = a - q * d;
+    if (r < 0) {
+        --q;
+        r += d;
+    } else if (r >= d) {
+        ++q;
+        r -= d;
+    }
+    return q + (r > 0);
+}
+
+__device__ __forceinline__ bool balanced_unit(const DecodeParams& p, int unit, int lane, int& b,
+                                              int& s, int& nsplit, int& vl_b) {
+    // Wave reductions on DPP rows and permlane swaps, carried in fp32: every
+    // value here is an integer below 2^24 (the plan bounds topk + swa), so
+    // the sums and maxima are exact.
+    auto wsum = [](int v) { return (int)xrow_sum4(row_sum16((float)v)); };
+    int eff = 0;
+    if (lane < p.B) {
+        const int vl = p.valid_len
+                           ? min(max(p.valid_len[fdiv((uint32_t)lane, p.fd_sq)], 0), p.topk)
+                           : p.topk;
+        eff = vl + p.swa;
+    }
+    const int emax = (int)xrow_max4(row_max16((float)eff));
+    int lo = max(1, ceil_div_small(emax, kTile * p.S));
+    int hi = p.bal_hi;
+    const int budget = p.B * p.bal;
+    auto splits_at = [&](int t) { return lane < p.B ? max(1, ceil_div_small(eff, kTile * t)) : 0; };
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (wsum(splits_at(mid)) <= budget)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    const int n = splits_at(lo);
+    // Inclusive prefix sum over the lanes: within each 16-lane row by DPP
+    // row shifts (lanes shifted in from outside the row read 0), then the
+    // totals of the rows below added from lanes 15, 31 and 47.
+    float x = (float)n;
+    x += dpp<0x111>(x);
+    x += dpp<0x112>(x);
+    x += dpp<0x114>(x);
+    x += dpp<0x118>(x);
+    const int xi = __builtin_bit_cast(int, x);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 15));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 31));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 47));
+    const int row = lane >> 4;
+    const int incl = (int)(x + (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f));
+    const uint64_t past = __builtin_amdgcn_ballot_w64(lane < p.B && incl > unit);
+    if (past == 0) return false;
+    const int t = (int)__builtin_ctzll(past);
+    nsplit = __builtin_amdgcn_readlane(n, t);
+    s = unit - (__builtin_amdgcn_readlane(incl, t) - nsplit);
+    b = t;
+    vl_b = __builtin_amdgcn_readlane(eff, t) - p.swa;   // no second load of the length
+    // Holds by construction; kept so that no index can leave the row's slots.
+    return s >= 0 && s < nsplit && nsplit <= p.S;
+}
+
 // The partial kernel's body.  SCRUB: non-finite dequantised elements read
 // as 0.  DENSE: rows come from a gathered bf16 buffer [B, idx_stride, 512]
 // with a per-entry mask (1 = takes no part) instead of the FP8 cache.
@@ -85,16 +161,23 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     const int g = (int)(r8 % p.G);
     const int64_t unit = (r8 / p.G) * kXcds + x;
     if (unit >= p.units) return;
-    const int b = (int)(unit / p.S);
-    const int s = (int)(unit % p.S);
+    int b, s, nsplit;                         // token, split, the token's split count
+    int vl = -1;                              // the token's valid length, once known
+    if (!DENSE && p.bal) {
+        if (!balanced_unit(p, (int)unit, lane, b, s, nsplit, vl)) return;
+    } else {
+        b = (int)(unit / p.S);
+        s = (int)(unit % p.S);
+        nsplit = p.S;
+    }
     const int seq = b / p.sq;                 // tokens of one sequence share its table and length
     const int h0 = g * HG;
 
     // This split's slice of the effective list main[0:vl] ++ swa, in chunks
     // rounded up to whole tiles.
-    const int vl = p.valid_len ? min(max(p.valid_len[seq], 0), p.topk) : p.topk;
+    if (vl < 0) vl = p.valid_len ? min(max(p.valid_len[seq], 0), p.topk) : p.topk;
     const int eff = vl + p.swa;
-    int chunk = (eff + p.S - 1) / p.S;
+    int chunk = (eff + nsplit - 1) / nsplit;
     chunk = (chunk + kTile - 1) / kTile * kTile;
     const int lo = min(s * chunk, eff);
     const int hi = min(lo + chunk, eff);
@@ -617,6 +700,14 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(Ob + h * kOLd + 8 * ch);
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + h * row_stride + 8 * ch));
     }
+    // Balanced splits: the token's last split marks the slots it leaves
+    // unused as empty (lse -inf), so the combine adds nothing from them.
+    // Stored last: stores count on the same counter as loads, so a store
+    // ahead of the kernel's loads would hold back every wait on them.
+    if (!DENSE && nsplit < p.S && s == nsplit - 1 && tid < HG) {
+        float* row = p.part_lse + ((int64_t)b * p.H + h0 + tid) * p.S;
+        for (int k = nsplit; k < p.S; ++k) row[k] = -INFINITY;
+    }
 }
 
 template <int HG, bool SCRUB, bool EMIT = false>
@@ -963,8 +1054,11 @@ hipError_t launch_decode_partial(const DecodeParams& p, int heads_per_group, int
                                  bool scrub, hipStream_t stream) {
     // The conversion output needs the block table, a single pool and at most
     // 1024 columns per split.
-    if (p.slots != nullptr &&
-        (p.bt == nullptr || p.kv2 != nullptr || (p.topk + p.swa + p.S - 1) / p.S > 2 * kThreads))
+    if (p.slots != nullptr && (p.bt == nullptr || p.kv2 != nullptr || p.bal != 0 ||
+                               (p.topk + p.swa + p.S - 1) / p.S > 2 * kThreads))
+        return hipErrorInvalidValue;
+    // Balanced splits: the batch's tokens fit one wave's lanes.
+    if (p.bal != 0 && (p.B > 64 || p.S < 2 || p.units != (int64_t)p.B * p.bal))
         return hipErrorInvalidValue;
     const dim3 g((unsigned)grid);
     return scrub ? launch_partial_variant<true>(p, heads_per_group, g, stream)

@@ -92,8 +92,12 @@ struct DecodeParams {
     int64_t bt_stride;
     int64_t page_stride;
     int64_t idx_stride;
-    int64_t units;              // B * S
+    int64_t units;              // work units: B * S, or B * bal with balanced splits
     int32_t B, H, topk, swa, bs, max_blocks, S, G;
+    // Balanced splits (pipelined kernel): 0 = off; else the split budget per
+    // token, with S the split slots per (token, head) row of the partials.
+    int32_t bal;
+    int32_t bal_hi;             // ceil(ceil((topk + swa) / bal) / 32): the uniform tiles per split
     int32_t sq;                 // query tokens per sequence (block-table row / valid_len entry)
     float qk_scale_log2;        // sm_scale * log2(e)
     // Launch-time divisors (the short-split kernel): splits, head groups,

@@ -80,7 +80,8 @@ def test_tokens_per_seq_must_divide_the_batch():
 def test_unknown_decode_flags_are_rejected():
     dsv4.dsv4_sparse_decode_plan(_desc(1, 64, 10, 0, flags=dsv4.DSV4_DECODE_SCRUB))
     dsv4.dsv4_sparse_decode_plan(_desc(1, 64, 10, 0, flags=dsv4.DSV4_DECODE_PIPELINED))
-    for bad in (0x4, 0x80000000):
+    dsv4.dsv4_sparse_decode_plan(_desc(1, 64, 10, 0, flags=dsv4.DSV4_DECODE_BALANCE))
+    for bad in (0x8, 0x80000000):
         assert _status(_desc(1, 64, 10, 0, flags=bad)) == dsv4.DSV4_ERR_INVALID_ARGUMENT
         assert "flags" in dsv4.dsv4_last_error()
 
@@ -391,3 +392,22 @@ def test_short_timeline_refuses_other_kernels_without_touching_the_gpu():
     st = dsv4._lib.dsv4_short_timeline(ctypes.byref(d), None, None, None, None, None, None, None,
                                       None, 0, None, None)
     assert st == dsv4.DSV4_ERR_NOT_SUPPORTED
+
+
+def test_make_pool_keeps_its_tensors_alive():
+    """The pool struct carries raw pointers; the binding keeps the tensors
+    they point into referenced for as long as the pool lives."""
+    import gc
+    import weakref
+    import torch
+    kv = torch.zeros((4, 64 * 584), dtype=torch.uint8)
+    bt = torch.zeros((2, 3), dtype=torch.int32)
+    refs = weakref.ref(kv), weakref.ref(bt)
+    pl = dsv4.make_pool(kv, bt, block_size=64, max_blocks_per_seq=3)
+    del kv, bt
+    gc.collect()
+    assert refs[0]() is not None and refs[1]() is not None
+    assert pl.kv_cache == refs[0]().data_ptr() and pl.num_blocks == 4
+    del pl
+    gc.collect()
+    assert refs[0]() is None and refs[1]() is None

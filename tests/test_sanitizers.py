@@ -110,20 +110,23 @@ static void need(bool c, const char* what) {
 static void decode_ok(const DecodeParams& p, int hg, int64_t grid) {
     need(p.B >= 1 && p.H % 16 == 0 && hg % 16 == 0 && p.H % hg == 0, "heads");
     need(p.G == p.H / hg, "head groups");
-    need(p.units == (int64_t)p.B * p.S, "units");
+    need(p.units == (int64_t)p.B * (p.bal ? p.bal : p.S), "units");
+    need(p.bal == 0 || (p.B <= 64 && p.bal >= 2 && p.S > p.bal), "balanced splits");
     need(grid >= p.units * p.G && grid % p.G == 0, "grid");
     need(p.S == 1 || (p.part_o && p.part_lse), "split workspace");
 }
 hipError_t launch_decode_partial(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
     decode_ok(p, hg, grid);
-    need(p.slots == nullptr || (p.bt != nullptr && (p.topk + p.swa + p.S - 1) / p.S <= 1024),
-         "slots need the block table and at most 1024 columns per split");
+    need(p.slots == nullptr || (p.bt != nullptr && p.bal == 0 &&
+                                (p.topk + p.swa + p.S - 1) / p.S <= 1024),
+         "slots need the block table, uniform splits and at most 1024 columns per split");
     ++g_launches; return hipSuccess;
 }
 hipError_t launch_decode_short(const DecodeParams& p, int hg, int64_t grid, bool, hipStream_t) {
     decode_ok(p, hg, grid);
     need(hg == 16 || hg == 32 || hg == 64, "short-kernel head group");
     need(p.slots == nullptr || p.bt != nullptr, "slots need the block table");
+    need(p.bal == 0, "balanced splits run on the pipelined kernel only");
     ++g_launches; return hipSuccess;
 }
 size_t short_lds_bytes(int) { return 0; }
@@ -156,6 +159,7 @@ CLIENT = r"""
 #include <stdio.h>
 #include <string.h>
 #include "dsv4.h"
+#include "dsv4_diag.h"
 
 int stub_launches(void);
 #define CHECK(c) do { if (!(c)) { printf("FAIL %s:%d %s (%s)\n", __FILE__, __LINE__, #c, \
@@ -226,6 +230,55 @@ int main(void) {
             }
         }
     }
+    /* Balanced splits: the same grid, S + ceil(S/4) split slots per row, only
+       on pipelined plans with S >= 2 and batch <= 64; the slot-writing decode
+       then converts in a launch of its own. */
+    for (i = 0; i < 5; ++i) {
+        dsv4_plan u;
+        base(&d, shapes[i][0], shapes[i][1], shapes[i][2], shapes[i][3]);
+        for (S = 0; S <= 64; S += (S < 4 ? 1 : 15)) {
+            int on, want;
+            d.flags = 0;
+            CHECK(dsv4_sparse_decode_plan(&d, S, &u) == DSV4_OK);
+            d.flags = DSV4_DECODE_BALANCE;
+            CHECK(dsv4_sparse_decode_plan(&d, S, &plan) == DSV4_OK);
+            on = u.partial_kernel == DSV4_KERNEL_PIPELINED && u.num_splits >= 2 && d.batch <= 64;
+            want = u.num_splits + (u.num_splits + 3) / 4;
+            if (want > DSV4_MAX_SPLITS) want = DSV4_MAX_SPLITS;
+            CHECK(plan.balanced_splits == (on ? u.num_splits : 0));
+            CHECK(plan.num_splits == (on ? want : u.num_splits));
+            CHECK(plan.grid_partial == u.grid_partial);
+            CHECK(plan.workspace_bytes ==
+                  (plan.num_splits > 1 ? (size_t)d.batch * d.num_heads * plan.num_splits * 1028 : 0));
+            d.workspace = plan.workspace_bytes ? DEV(0x10000) : NULL;
+            d.workspace_bytes = plan.workspace_bytes;
+            CHECK(dsv4_sparse_decode(&d, DEV(0x1000), DEV(0x2000), (const int32_t*)DEV(0x3000),
+                                     (const int32_t*)DEV(0x4000), (const int32_t*)DEV(0x9000),
+                                     (const float*)DEV(0x5000), DEV(0x6000), (float*)DEV(0x7000),
+                                     S, NULL) == DSV4_OK);
+            n += plan.num_splits > 1 ? 2 : 1;
+            CHECK(stub_launches() == n);
+            CHECK(dsv4_sparse_decode_with_slots(&d, DEV(0x1000), DEV(0x2000),
+                                                (const int32_t*)DEV(0x3000),
+                                                (const int32_t*)DEV(0x4000), NULL, NULL,
+                                                DEV(0x6000), NULL, S, (int32_t*)DEV(0x8000),
+                                                NULL) == DSV4_OK);
+            {
+                const int kt = shapes[i][2] + shapes[i][3];
+                const int conv = plan.partial_kernel != DSV4_KERNEL_SHORT &&
+                                 (on || (kt + plan.num_splits - 1) / plan.num_splits > 1024);
+                n += (plan.num_splits > 1 ? 2 : 1) + conv;
+                CHECK(stub_launches() == n);
+            }
+            if (on)
+                CHECK(dsv4_gather_floor(&d, DEV(0x2000), (const int32_t*)DEV(0x3000),
+                                        (const int32_t*)DEV(0x4000), NULL, S,
+                                        (uint32_t*)DEV(0xA000), NULL) == DSV4_ERR_INVALID_ARGUMENT);
+            CHECK(stub_launches() == n);
+        }
+    }
+    d.flags = 0;
+
     /* Validation errors never launch. */
     base(&d, 1, 64, 2048, 0);
     d.num_heads = 24;   CHECK(dsv4_sparse_decode_plan(&d, 0, &plan) == DSV4_ERR_INVALID_ARGUMENT);
