@@ -25,10 +25,10 @@ def _gh():
     return gpu_helpers
 
 
-def _both(w, S):
+def _both(w, S, flags=0):
     gh = _gh()
     dw = gh.DeviceWorkload(w)
-    desc = gh.make_desc(w)
+    desc = gh.make_desc(w, flags=flags)
     nbytes = dsv4.dsv4_sparse_decode_workspace_bytes(desc, S)
     assert nbytes <= dsv4.NOALLOC_SCRATCH_BYTES
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
@@ -37,11 +37,11 @@ def _both(w, S):
         out = torch.full((w.B, w.H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
         lse = torch.full((w.B, w.H), float("nan"), dtype=torch.float32, device="cuda")
         if noalloc:
-            dsv4.dsv4_sparse_decode_noalloc(gh.make_desc(w), dw.q, dw.kv, dw.bt, dw.idx, dw.vl,
-                                            dw.sink, out, lse, S)
+            dsv4.dsv4_sparse_decode_noalloc(gh.make_desc(w, flags=flags), dw.q, dw.kv, dw.bt,
+                                            dw.idx, dw.vl, dw.sink, out, lse, S)
         else:
-            dsv4.dsv4_sparse_decode(gh.make_desc(w, workspace=ws), dw.q, dw.kv, dw.bt, dw.idx,
-                                    dw.vl, dw.sink, out, lse, S)
+            dsv4.dsv4_sparse_decode(gh.make_desc(w, workspace=ws, flags=flags), dw.q, dw.kv,
+                                    dw.bt, dw.idx, dw.vl, dw.sink, out, lse, S)
         torch.cuda.synchronize()
         outs.append((out, lse))
     return outs, nbytes
@@ -67,6 +67,26 @@ def test_noalloc_decode_matches_the_workspace_decode():
         gh.assert_decode_close(o.float().double().cpu().numpy(), l.double().cpu().numpy(),
                                ro, rl, what)
     assert sizes[0] > sizes[1] > 0 and sizes[2] == 0
+
+
+def test_noalloc_with_balanced_splits():
+    """DSV4_DECODE_BALANCE sizes the scratch use by the split slots; the
+    result matches the workspace decode bit for bit, twice in a row (the
+    second call smaller, with fewer tokens)."""
+    gh = _gh()
+    flags = dsv4.DSV4_DECODE_BALANCE | dsv4.DSV4_DECODE_PIPELINED
+    for B, seed in ((6, 520), (3, 521)):
+        w = make_custom(B=B, H=64, topk=512, swa=64, seq_lens=[4000 + 500 * b for b in range(B)],
+                        seed=seed, invalid_frac=0.03, valid_len_range=(20, 512))
+        plan = dsv4.dsv4_sparse_decode_plan(gh.make_desc(w, flags=flags), 4)
+        assert plan.balanced_splits == 4 and plan.num_splits == 5
+        print(f"noalloc balanced B={B}", flush=True)
+        ((o_ref, l_ref), (o, l)), _ = _both(w, 4, flags)
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+        assert torch.equal(l, l_ref)
+        ro, rl, _ = oracle.decode_workload(w)
+        gh.assert_decode_close(o.float().double().cpu().numpy(), l.double().cpu().numpy(),
+                               ro, rl, f"noalloc balanced B={B}")
 
 
 def test_noalloc_refuses_a_decode_larger_than_its_scratch():
