@@ -1,7 +1,8 @@
 """Seeded random decode cases on the GPU, mixing features the targeted tests
 cover one at a time: head counts 16-128 (every head-group variant), forced
 and selected split counts, block sizes, masked tails, invalid entries,
-several query tokens per sequence and a separate SWA pool.  Each case is
+several query tokens per sequence, a separate SWA pool, the pipelined
+kernel forced and balanced splits (DSV4_DECODE_BALANCE).  Each case is
 compared with the oracle to the decode tolerance (|d out| <= 2e-2 +
 1e-2 |out_ref|, |d lse| <= 1e-3)."""
 
@@ -34,19 +35,21 @@ def _case(seed):
     dual = swa > 0 and rng.random() < 0.4
     if dual:
         w = split_swa_pool(w, block_size=int(rng.choice([1, 16, 64])), seed=seed + 1)
-    return w, S, dual
+    flags = ((dsv4.DSV4_DECODE_BALANCE if rng.random() < 0.4 else 0)
+             | (dsv4.DSV4_DECODE_PIPELINED if rng.random() < 0.3 else 0))
+    return w, S, dual, flags
 
 
-@pytest.mark.parametrize("seed", range(300, 316))
+@pytest.mark.parametrize("seed", range(300, 332))
 def test_random_case(seed):
     from tests import gpu_helpers as gh
-    w, S, dual = _case(seed)
+    w, S, dual, flags = _case(seed)
     print(f"random seed={seed} B={w.B} H={w.H} topk={w.topk} swa={w.swa} bs={w.block_size} "
-          f"s_q={w.s_q} S={S} dual={dual}", flush=True)
-    desc = gh.make_desc(w)
+          f"s_q={w.s_q} S={S} dual={dual} flags={flags}", flush=True)
+    desc = gh.make_desc(w, flags=flags)
     n = dsv4.dsv4_sparse_decode_workspace_bytes(desc, S)
     ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
-    desc = gh.make_desc(w, workspace=ws)
+    desc = gh.make_desc(w, workspace=ws, flags=flags)
     dw = gh.DeviceWorkload(w)
     out = torch.full((w.B, w.H, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((w.B, w.H), float("nan"), dtype=torch.float32, device="cuda")
