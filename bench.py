@@ -35,6 +35,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -89,11 +90,17 @@ def _parse():
 
 
 def _source_digest() -> str:
+    """Digest of the decode kernels' sources with comments and whitespace
+    removed, so that an edit to a comment does not orphan the counters taken
+    on the same code."""
     h = hashlib.sha256()
     for name in ("decode.hip", "decode_short.hip", "decode_common.hpp",
                  "device_util.hpp", "fastdiv.hpp", "internal.hpp"):
-        with open(os.path.join(ROOT, "sparse_mla_attention_block_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_mla_attention_block_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -33,7 +33,10 @@
 // NaN in the cache can never reach an MFMA.  The running sum takes the fp32
 // probabilities, the PV operand their bf16 rounding.  With one split the
 // epilogue folds the sink in and writes bf16 output and lse; with several it
-// writes the split's normalised bf16 partial and lse.
+// writes the split's normalised bf16 partial and lse.  Output rows are staged
+// in LDS and leave as whole 1 KB rows (16-byte nontemporal stores).
+// Work units are (token, split) pairs; with balanced splits each token's
+// split count follows its run-time length (balanced_unit below).
 // Variants of the same body: SCRUB zeroes non-finite dequantised elements;
 // DENSE reads already gathered bf16 rows with a mask (two tiles in flight, as
 // a 1 KB row needs 32 registers per producer lane); a dual cache resolves

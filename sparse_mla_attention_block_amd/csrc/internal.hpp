@@ -106,9 +106,10 @@ struct DecodeParams {
     // Measurement aid (short-split kernel only): per-workgroup phase stamps,
     // kTimelineStamps words per workgroup, or null.
     uint64_t* timeline;
-    // Short-split kernel with a block table only: the req-local -> global
-    // conversion of every index column, int32 [B, topk + swa], fill -1; or
-    // null.
+    // Either partial kernel, with a block table and uniform splits (the
+    // pipelined one with at most 1024 index columns a split): the req-local
+    // -> global conversion of every index column, int32 [B, topk + swa],
+    // fill -1; or null.
     int32_t* slots;
 };
 
