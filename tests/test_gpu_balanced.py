@@ -109,6 +109,7 @@ def test_ragged_workload_balanced():
     (3, 128, 1024, 0, 0, [1024, 40, 600]),               # selector's S, no SWA
     (5, 32, 384, 32, 7, [384, 384, 384, 384, 384]),      # equal lengths
     (2, 64, 256, 0, 2, [0, 0]),                          # nothing to attend
+    (4, 64, 640, 32, 3, [-7, 100000, 320, 1]),           # lengths clamped to [0, topk]
 ])
 def test_balanced_small_cases(B, H, topk, swa, S, vl):
     w = make_custom(B=B, H=H, topk=topk, swa=swa, seq_lens=[5000 + 321 * b for b in range(B)],
