@@ -540,6 +540,8 @@ def profile_workload(ci: int, steps: int) -> int:
     dk = dict(batch=w.B, num_heads=w.H, topk=w.topk, swa=w.swa, block_size=w.block_size,
               num_blocks=w.num_blocks, page_stride=w.page_stride, sm_scale=w.sm_scale,
               max_blocks_per_seq=w.max_blocks_per_seq, block_table_stride=w.block_table.shape[1])
+    if w.per_row_splits:                       # the configuration's per-row split count
+        dk["flags"] = dsv4.DSV4_DECODE_BALANCE
     plan = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**dk), w.num_splits)
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
     desc = dsv4.make_desc(workspace=ws, **dk)
@@ -553,7 +555,7 @@ def profile_workload(ci: int, steps: int) -> int:
     print(json.dumps({"workload": w.name, "valid_entries": n_valid,
                       "algorithmic_flops": n_valid * 2048 * w.H,
                       "heads_per_group": plan.heads_per_group, "num_splits": plan.num_splits,
-                      "launches": steps}), flush=True)
+                      "balanced_splits": plan.balanced_splits, "launches": steps}), flush=True)
     return 0
 
 
@@ -612,11 +614,14 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
                   num_blocks=R * nb, page_stride=stride, sm_scale=w.sm_scale,
                   max_blocks_per_seq=w.max_blocks_per_seq,
                   block_table_stride=w.block_table.shape[1], tokens_per_seq=w.s_q)
-        plan = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**kw), w.num_splits)
+        # The ragged batch's configuration chooses the split count per row:
+        # balanced splits (the uniform selector plan is timed beside it).
+        flags = dsv4.DSV4_DECODE_BALANCE if w.per_row_splits else 0
+        plan = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(flags=flags, **kw), w.num_splits)
         ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
               if plan.workspace_bytes else None)
-        desc = dsv4.make_desc(workspace=ws, **kw)
-        desc_pipe = dsv4.make_desc(workspace=ws, flags=dsv4.DSV4_DECODE_PIPELINED, **kw)
+        desc = dsv4.make_desc(workspace=ws, flags=flags, **kw)
+        desc_pipe = dsv4.make_desc(workspace=ws, flags=flags | dsv4.DSV4_DECODE_PIPELINED, **kw)
         kv = pool.view(-1)
 
         def timed(rot, d=desc, S=w.num_splits):
@@ -659,31 +664,29 @@ def workloads_leg(dev, K=100, pool_cap_bytes=8 << 30):
                 "warm_us": timed(False, desc, 4), "cold_us": timed(True, desc, 4)}}
         nbytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * (512 * 2 * 2 + 4)
         flops = n_valid * 2048 * H
-        # Tokens of different lengths: the same decode with balanced splits
-        # (DSV4_DECODE_BALANCE), split counts following each token's length.
-        bal = {}
-        if w.valid_len is not None:
-            kwb = dict(kw, flags=dsv4.DSV4_DECODE_BALANCE)
-            planb = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**kwb), w.num_splits)
-            if planb.balanced_splits:
-                wsb = torch.empty(planb.workspace_bytes, dtype=torch.uint8, device=dev)
-                descb = dsv4.make_desc(workspace=wsb, **kwb)
-                bw, bc = timed(False, descb), timed(True, descb)
-                bal = {"balanced_plan": {
-                    "split_budget": planb.balanced_splits, "split_slots": planb.num_splits,
-                    "warm_us": bw, "cold_us": bc,
-                    "GBps": nbytes / (bc * 1e-6) / 1e9,
-                    "frac_hbm": nbytes / (bc * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                    "TFLOPs": flops / (bc * 1e-6) / 1e12,
-                    "frac_mfma": flops / (bc * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}}
-                del wsb
+        # Per-row split counts: the uniform selector plan of the same decode.
+        uni = {}
+        if w.per_row_splits:
+            planu = dsv4.dsv4_sparse_decode_plan(dsv4.make_desc(**kw), w.num_splits)
+            wsu = (torch.empty(planu.workspace_bytes, dtype=torch.uint8, device=dev)
+                   if planu.workspace_bytes else None)
+            descu = dsv4.make_desc(workspace=wsu, **kw)
+            uw, uc = timed(False, descu), timed(True, descu)
+            uni = {"uniform_plan": {
+                "num_splits": planu.num_splits, "warm_us": uw, "cold_us": uc,
+                "GBps": nbytes / (uc * 1e-6) / 1e9,
+                "frac_hbm": nbytes / (uc * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                "TFLOPs": flops / (uc * 1e-6) / 1e12,
+                "frac_mfma": flops / (uc * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}}
+            del wsu
         gbps = nbytes / (cold_us * 1e-6) / 1e9
         tflops = flops / (cold_us * 1e-6) / 1e12
         res.append({
             "workload": w.name, "B": B, "H": H, "topk": w.topk, "swa": w.swa,
             "valid_entries": n_valid, "heads_per_group": plan.heads_per_group,
             "num_splits": plan.num_splits, "grid_partial": plan.grid_partial,
-            "partial_kernel": kname, **pipe, **cap4, **bal,
+            "partial_kernel": kname, "balanced_splits": plan.balanced_splits,
+            **pipe, **cap4, **uni,
             "replicas": R, "MB_between_reuse": round(R * touched / 1e6, 1),
             "warm_us": warm_us, "cold_us": cold_us,
             "tokens_per_s": n_valid / (cold_us * 1e-6),

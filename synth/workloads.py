@@ -44,7 +44,8 @@ POISON = 0xFF
 # The five decode workloads.  ``seq_len`` is ("fixed", L) or
 # ("loguniform", lo, hi); ``invalid_frac`` is the share of main top-k
 # positions set to -1; ``valid_len`` is None or an inclusive (lo, hi) range
-# for the per-row length of the main list.
+# for the per-row length of the main list; ``per_row_splits``: the split
+# count is chosen per row from the lengths (the ragged batch's configuration).
 CONFIGS = [
     dict(name="tiny", B=1, H=16, topk=128, swa=0, seq_len=("fixed", 2048),
          invalid_frac=0.05, valid_len=None, num_splits=1),
@@ -55,7 +56,7 @@ CONFIGS = [
     dict(name="large_batch", B=256, H=64, topk=512, swa=128, seq_len=("fixed", 8192),
          invalid_frac=0.0, valid_len=None, num_splits=0),
     dict(name="ragged", B=32, H=128, topk=2048, swa=128, seq_len=("loguniform", 1024, 65536),
-         invalid_frac=0.05, valid_len=(1024, 2048), num_splits=0),
+         invalid_frac=0.05, valid_len=(1024, 2048), num_splits=0, per_row_splits=True),
 ]
 
 
@@ -87,6 +88,8 @@ class Workload:
     # A second pool for the SWA entries (dict: kv, block_table, block_size,
     # num_blocks, page_stride, max_blocks_per_seq), or None: one pool.
     swa_pool: Optional[dict] = None
+    # The workload's configuration asks for a split count chosen per row.
+    per_row_splits: bool = False
 
     @property
     def Kt(self) -> int:
@@ -232,7 +235,9 @@ def make_workload(config: int, *, seed: Optional[int] = None, block_size: int = 
               block_size=block_size, invalid_frac=c["invalid_frac"],
               valid_len_range=c["valid_len"], num_splits=c["num_splits"], name=c["name"], rng=rng)
     kw.update(overrides)
-    return make_custom(**kw)
+    w = make_custom(**kw)
+    w.per_row_splits = bool(c.get("per_row_splits", False))
+    return w
 
 
 def workload_digest(w: Workload) -> str:

@@ -42,8 +42,19 @@ def _check(w, what, **gpu_kw):
 
 @pytest.mark.parametrize("ci", range(5))
 def test_workload_full_size(ci):
+    """At the benchmark's plan: the selector's split count, with the split
+    count chosen per row (balanced splits) where the configuration asks for
+    it (the ragged batch)."""
     w = make_workload(ci)
-    _check(w, f"workload {ci} {w.name}")
+    flags = dsv4.DSV4_DECODE_BALANCE if w.per_row_splits else 0
+    _check(w, f"workload {ci} {w.name}", flags=flags)
+
+
+def test_ragged_workload_with_uniform_splits():
+    """The ragged batch at the selector's uniform plan as well."""
+    w = make_workload(4)
+    assert w.per_row_splits
+    _check(w, "workload 4 ragged, uniform splits")
 
 
 @pytest.mark.parametrize("S", [4, 2, 3])
