@@ -61,9 +61,10 @@ namespace dsv4 {
 // holds it; units past the last token's splits have no work.  Every wave
 // computes the same assignment.  (vLLM PR #52212 page, implementation item
 // 2: a fixed grid whose rows pick their active splits at run time.)
-// ceil(a / d) for 0 <= a < 2^24 and 32 <= d < 2^24: a/d < 2^19, so the
-// quotient from the fp32 reciprocal (relative error below 2^-21) is within
-// one of the exact one, and one integer correction step fixes it.
+// ceil(a / d) for 0 <= a <= 2^24 and 32 <= d < 2^24: a and d are exact in
+// fp32 and a/d <= 2^19, so the quotient from the fp32 reciprocal (relative
+// error below 2^-21) is within one of the exact one, and one integer
+// correction step fixes it.
 __device__ __forceinline__ int ceil_div_small(int a, int d) {
     int q = (int)((float)a * __builtin_amdgcn_rcpf((float)d));
     int r = a - q * d;
@@ -80,8 +81,8 @@ __device__ __forceinline__ int ceil_div_small(int a, int d) {
 __device__ __forceinline__ bool balanced_unit(const DecodeParams& p, int unit, int lane, int& b,
                                               int& s, int& nsplit, int& vl_b) {
     // Wave reductions on DPP rows and permlane swaps, carried in fp32: every
-    // value here is an integer below 2^24 (the plan bounds topk + swa), so
-    // the sums and maxima are exact.
+    // value here is an integer of at most 2^24 (the plan bounds topk + swa),
+    // so the sums and maxima are exact.
     auto wsum = [](int v) { return (int)xrow_sum4(row_sum16((float)v)); };
     int eff = 0;
     if (lane < p.B) {
