@@ -194,6 +194,22 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     const int hc = 16 * wave + l16;              // consumer lane's head (within the group)
     auto meta_tile = [&](int t) { return meta + (t % kMetaTiles) * kTile * 2; };
     auto kbuf = [&](int t) { return Kn + (t % kKBufs) * (kTile * kD); };
+    // LDS fragment offsets (elements) split into a per-lane part, fixed for
+    // the kernel, and the K buffer's offset, held in a scalar register, so
+    // that each fragment address costs one add per step.  QK: k-steps ks and
+    // ks + 8 differ by 256 elements, rows 16 + r and r by 16 rows (the
+    // swizzle only moves unit bits 1-4 and depends on row bits 0-3).
+    int kq[8], kvo[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kq[i] = kofs(l16, 32 * i + 8 * lg);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+        kvo[nt] = kofs(4 * lg + (l16 >> 2), 64 * wave + 16 * nt + 4 * (l16 & 3));
+    auto kbase = [&](int t) __attribute__((always_inline)) {
+        int kb = (t % kKBufs) * (kTile * kD);
+        asm volatile("" : "+s"(kb));
+        return kb;
+    };
 
     // One 64-register array per lane, used by role: consumers keep the q
     // row of their head in it (lane (l16, lg) holds dims 32*ks + 8*lg .. +7
@@ -435,18 +451,16 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         }
     };
     auto pv_mma = [&](int k) __attribute__((always_inline)) {
-        const __bf16* K = kbuf(k);
+        const int kb = kbase(k);
         const __bf16* P = Pb + (k & 1) * (HG * kPLd);
         bf16x8 pa[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             pa[mt] = *reinterpret_cast<const bf16x8*>(&P[(16 * mt + l16) * kPLd + 8 * lg]);
-        const int vr = 4 * lg + (l16 >> 2);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const int d = 64 * wave + 16 * nt + 4 * (l16 & 3);
-            const i16x4 v0 = lds_read_tr16(K + kofs(vr, d));
-            const i16x4 v1 = lds_read_tr16(K + kofs(16 + vr, d));
+            const i16x4 v0 = lds_read_tr16(Kn + (kb + kvo[nt]));
+            const i16x4 v1 = lds_read_tr16(Kn + (kb + kvo[nt]) + 16 * kD);
             const bf16x8 vb = __builtin_bit_cast(
                 bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -470,20 +484,21 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         // Four accumulator chains (rows 0-15 / 16-31, even / odd k-steps);
         // K fragments are read four k-steps ahead of their MFMAs, an order
         // pinned with scheduling-group barriers so LDS latency stays hidden.
-        const __bf16* K = kbuf(t);
+        const int kb = kbase(t);
         f32x4 sa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4 sb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         // Lane (l16, lg) reads rows l16 and 16 + l16 (same swizzle), elements
         // 32ks + 8lg.
-        auto kfrag = [&](int row, int ks) {
-            return *reinterpret_cast<const bf16x8*>(K + kofs(row, 32 * ks + 8 * lg));
+        auto kfrag = [&](int rb, int ks) {
+            return *reinterpret_cast<const bf16x8*>(Kn + (kb + kq[ks & 7]) + 256 * (ks >> 3) +
+                                                    16 * kD * rb);
         };
         constexpr int kAhead = 6;
         bf16x8 fa[kAhead], fb[kAhead];
 #pragma unroll
         for (int ks = 0; ks < kAhead; ++ks) {
-            fa[ks] = kfrag(l16, ks);
-            fb[ks] = kfrag(16 + l16, ks);
+            fa[ks] = kfrag(0, ks);
+            fb[ks] = kfrag(1, ks);
         }
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
@@ -494,8 +509,8 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             sb[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[ks % kAhead], qb, sb[ks & 1],
                                                                  0, 0, 0);
             if (ks + kAhead < 16) {
-                fa[ks % kAhead] = kfrag(l16, ks + kAhead);
-                fb[ks % kAhead] = kfrag(16 + l16, ks + kAhead);
+                fa[ks % kAhead] = kfrag(0, ks + kAhead);
+                fb[ks % kAhead] = kfrag(1, ks + kAhead);
             }
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);     // DS reads
