@@ -332,8 +332,6 @@ int decode_impl(const dsv4_decode_desc* d, const void* q, const void* kv, const 
         if (sh.short_kernel || (!sh.bal && ceil_div(sh.kt, sh.splits) <= 2 * dsv4::kThreads)) {
             p.slots = slots;
         } else {
-            if (sh.kt > 65535 * 256)
-                return fail(DSV4_ERR_INVALID_ARGUMENT, "topk + swa too large for the conversion");
             dsv4::ConvertParams c;
             c.req_id = nullptr;
             c.bt = bt;
@@ -544,7 +542,6 @@ int dsv4_convert_req_index_to_global(const int32_t* req_id, int32_t num_reqs,
     if (num_tokens < 0 || width < 0)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "num_tokens and width must be >= 0");
     if (num_tokens == 0 || width == 0) return ok();
-    if (width > 65535 * 256) return fail(DSV4_ERR_INVALID_ARGUMENT, "width too large");
     if (!block_table || !token_indices || !out)
         return fail(DSV4_ERR_INVALID_ARGUMENT, "block_table, token_indices and out must not be NULL");
     if (block_size < 1) return fail(DSV4_ERR_INVALID_ARGUMENT, "block_size must be >= 1");

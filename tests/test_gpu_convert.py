@@ -50,3 +50,22 @@ def test_workload_index_lists_bit_exact(ci):
     print(f"convert workload {ci} {w.name}", flush=True)
     got, want = _both(**kw)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_rows_wider_than_one_grid_of_column_tiles(ragged):
+    """Rows of 65535 x 256 + 1000 columns: more 256-column tiles than one grid
+    dimension holds, so the kernel walks the columns in grid strides."""
+    width = 65535 * 256 + 1000
+    rng = np.random.default_rng(4242 + ragged)
+    bs, mb, T = 64, 512, 2
+    bt = rng.integers(-1, 1 << 20, size=(3, mb)).astype(np.int32)
+    ti = rng.integers(-2, bs * mb + 100, size=(T, width)).astype(np.int32)
+    kw = dict(token_indices=ti, block_table=bt, max_blocks_per_req=mb, block_size=bs,
+              invalid_fill=-1, req_id=np.array([2, 0], dtype=np.int32), num_reqs=3)
+    if ragged:
+        kw["cu_seqlens"] = np.array([0, width - 7, 2 * width - 300], dtype=np.int32)
+        kw["width"] = width
+    print(f"convert width={width} ragged={ragged}", flush=True)
+    got, want = _both(**kw)
+    assert np.array_equal(got, want)
