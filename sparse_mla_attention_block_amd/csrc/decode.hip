@@ -482,8 +482,10 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
     auto qk_scores = [&](int t) __attribute__((always_inline)) -> Scores {
         // S^T = K q^T: A operand = K rows (entries), B operand = q (heads).
         // Four accumulator chains (rows 0-15 / 16-31, even / odd k-steps);
-        // K fragments are read four k-steps ahead of their MFMAs, an order
-        // pinned with scheduling-group barriers so LDS latency stays hidden.
+        // K fragments are read four k-steps ahead of their MFMAs, one read
+        // issued after each MFMA, an order pinned with scheduling-group
+        // barriers so LDS latency stays hidden (six k-steps ahead, or pairs
+        // of reads after pairs of MFMAs, measured 1-2 % slower).
         const int kb = kbase(t);
         f32x4 sa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4 sb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -493,7 +495,7 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
             return *reinterpret_cast<const bf16x8*>(Kn + (kb + kq[ks & 7]) + 256 * (ks >> 3) +
                                                     16 * kD * rb);
         };
-        constexpr int kAhead = 6;
+        constexpr int kAhead = 4;
         bf16x8 fa[kAhead], fb[kAhead];
 #pragma unroll
         for (int ks = 0; ks < kAhead; ++ks) {
@@ -515,9 +517,9 @@ __device__ __forceinline__ void decode_partial_body(const DecodeParams& p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);     // DS reads
 #pragma unroll
-        for (int ks = 0; ks < 16 - kAhead; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);            // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // DS reads
+        for (int ks = 0; ks < 2 * (16 - kAhead); ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS reads
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
         return Scores{sa[0] + sa[1], sb[0] + sb[1]};
