@@ -405,6 +405,16 @@ def main() -> int:
     part_bytes = n_valid * (ROW_BYTES + INDEX_BYTES) + B * H * 512 * 2
     step_bytes = part_bytes + B * H * (512 * 2 + 4)
     flops = n_valid * 2048 * H
+    # A plain device copy of the partial kernel's algorithmic bytes, its
+    # sources rotated so that every launch reads HBM: what one launch that
+    # moves this little data takes without any dependent loads.
+    crep = max(2, math.ceil(2 * INFINITY_CACHE_BYTES / part_bytes))
+    csrc = torch.empty(crep * part_bytes, dtype=torch.uint8, device=dev)
+    csrc.fill_(1)
+    cdst = torch.empty(part_bytes, dtype=torch.uint8, device=dev)
+    kt_copy_small = time_graph(capture(
+        lambda r: cdst.copy_(csrc[(r % crep) * part_bytes:(r % crep + 1) * part_bytes]), K), K)
+    del csrc, cdst
     tokens_per_s = n_valid / (ms_per_step * 1e-3)
     achieved = part_bytes / (kt_part * 1e-3) / 1e9
     digest = _source_digest()
@@ -455,7 +465,10 @@ def main() -> int:
         "kernels_ms": {"convert": kt_conv, "decode_partial": kt_part, "combine": kt_comb,
                        "decode_partial_global_slots": kt_part_slots},
         "floors_ms": {"gather_only": kt_gather, "empty_launch": kt_empty,
-                      "partial_over_gather": kt_part / kt_gather},
+                      "partial_over_gather": kt_part / kt_gather,
+                      "copy_of_partial_bytes": kt_copy_small,
+                      "copy_of_partial_bytes_frac": part_bytes / (kt_copy_small * 1e-3) / 1e9
+                      / HBM_PEAK_GBPS},
         "measured_copy_GBps": copy_GBps,
         "b_sweep": sweep,
         "split_sweep": split_sweep,
