@@ -2,7 +2,8 @@
 cover one at a time: head counts 16-128 (every head-group variant), forced
 and selected split counts, block sizes, masked tails, invalid entries,
 several query tokens per sequence, a separate SWA pool, the pipelined
-kernel forced and balanced splits (DSV4_DECODE_BALANCE).  Each case is
+kernel forced, balanced splits (DSV4_DECODE_BALANCE) and the scrub
+variants (DSV4_DECODE_SCRUB, on caches with no non-finite element).  Each case is
 compared with the oracle to the decode tolerance (|d out| <= 2e-2 +
 1e-2 |out_ref|, |d lse| <= 1e-3)."""
 
@@ -37,10 +38,12 @@ def _case(seed):
         w = split_swa_pool(w, block_size=int(rng.choice([1, 16, 64])), seed=seed + 1)
     flags = ((dsv4.DSV4_DECODE_BALANCE if rng.random() < 0.4 else 0)
              | (dsv4.DSV4_DECODE_PIPELINED if rng.random() < 0.3 else 0))
+    # The scrub variants on finite caches give the plain decode's result.
+    flags |= dsv4.DSV4_DECODE_SCRUB if rng.random() < 0.25 else 0
     return w, S, dual, flags
 
 
-@pytest.mark.parametrize("seed", range(300, 332))
+@pytest.mark.parametrize("seed", range(300, 348))
 def test_random_case(seed):
     from tests import gpu_helpers as gh
     w, S, dual, flags = _case(seed)
