@@ -370,8 +370,11 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
         row_stride = (int64_t)p.S * kD;
     }
     // The scaled accumulators are staged as bf16 rows in the (now free) K
-    // tile, then written with 16-byte nontemporal stores, one contiguous 1 KB
-    // head row per wave instruction.
+    // tile, then written with 16-byte stores, one contiguous 1 KB head row per
+    // wave instruction: nontemporal for the final output, ordinary for the
+    // split partials, which the combine reads right after (ordinary stores
+    // made the two-launch step 3 % faster; the pipelined kernel's larger
+    // partials measured the other way).
     static_assert(HG <= kShortRows && HG * 64 % kThreads == 0, "output staging");
     __bf16* obase = Kt + l16 * kShortLd + 64 * wave + 4 * lg;
 #pragma unroll
@@ -393,7 +396,11 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
         const int c = tid + k * kThreads;
         const int h = c >> 6, ch = c & 63;
         const u32x4 v = *reinterpret_cast<const u32x4*>(Kt + h * kShortLd + 8 * ch);
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + h * row_stride + 8 * ch));
+        u32x4* o = reinterpret_cast<u32x4*>(dst + h * row_stride + 8 * ch);
+        if (direct)
+            __builtin_nontemporal_store(v, o);
+        else
+            *o = v;
     }
     if constexpr (STAMPS) {
         mark(8, false);
