@@ -104,6 +104,24 @@ def _source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def _one_super_tile(plan, kt: int) -> bool:
+    """The short-split kernel's variant for splits of at most one 64-row
+    super-tile (chunks are whole 32-entry tiles)."""
+    chunk = -(-kt // plan.num_splits)
+    return -(-chunk // 32) * 32 <= 64
+
+
+def _partial_kernel_name(plan, kt: int, scrub: bool) -> str:
+    """The partial kernel one slot-writing decode launches, as rocprofv3 names it."""
+    import sparse_mla_attention_block_amd as dsv4
+    sc = "true" if scrub else "false"
+    if plan.partial_kernel == dsv4.DSV4_KERNEL_SHORT:
+        one = "true" if _one_super_tile(plan, kt) else "false"
+        return f"decode_short_kernel<{plan.heads_per_group}, {sc}, true, false, true, {one}>"
+    emit = "true" if not plan.balanced_splits and -(-kt // plan.num_splits) <= 1024 else "false"
+    return f"decode_partial_kernel<{plan.heads_per_group}, {sc}, {emit}>"
+
+
 def _traffic_from_profile(digest: str, kernel: str):
     """HBM bytes per launch of the partial kernel from the committed counter
     summary, if it was taken on the current kernel source and kernel variant."""
@@ -418,11 +436,7 @@ def main() -> int:
     tokens_per_s = n_valid / (ms_per_step * 1e-3)
     achieved = part_bytes / (kt_part * 1e-3) / 1e9
     digest = _source_digest()
-    kname = (("decode_short_kernel" if plan_tbl.partial_kernel == dsv4.DSV4_KERNEL_SHORT
-              else "decode_partial_kernel")
-             + f"<{plan_tbl.heads_per_group}, {'true' if args.scrub else 'false'}"
-             + (", true, false, true>" if plan_tbl.partial_kernel == dsv4.DSV4_KERNEL_SHORT
-                else ">"))
+    kname = _partial_kernel_name(plan_tbl, w.topk + w.swa, args.scrub)
     traffic = None if args.scrub else _traffic_from_profile(digest, kname)
 
     rec = {
@@ -528,8 +542,9 @@ def short_timeline(dsv4, desc, plan, q, kv, bt_all, B, idx, sink, out, lse, S, R
     names = ["resolve_and_issue", "dequant_st0", "barrier_wait", "qk", "softmax", "pv_and_rest",
              "epilogue"]
     phases = {n: int(np.median(t[:, k + 2] - t[:, k + 1])) for k, n in enumerate(names)}
-    return {"kernel": f"decode_short_kernel<{plan.heads_per_group}, false, true, true> "
-                      "(stamped variant)",
+    one = "true" if _one_super_tile(plan, idx.shape[1]) else "false"
+    return {"kernel": f"decode_short_kernel<{plan.heads_per_group}, false, true, true, false, "
+                      f"{one}> (stamped variant)",
             "workgroups": int(t.shape[0]), "clock_MHz": mhz,
             "wg_span_us_median": float(np.median(real)) / 100.0,
             "wg_start_spread_us": float(t[:, 0].max() - t[:, 0].min()) / 100.0,
