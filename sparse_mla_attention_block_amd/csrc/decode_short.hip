@@ -189,8 +189,8 @@ __global__ __launch_bounds__(kThreads) void decode_short_kernel(const DecodePara
     // The sink is loaded unconditionally here and used in the epilogue.
     const float sink_raw = *global(p.sink ? p.sink + h0 + (sm_active ? sm_h : 0) : &kZeroFloat);
 
-    // Table words, then the rows of both super-tiles (zero rows past the
-    // split's end), all unconditional.
+    // Table words, then the rows of both super-tiles (of the one, with ONE;
+    // zero rows past the split's end), all unconditional.
     const int32_t w0 = table_word<TABLE>(p, seq, i0);
     const int32_t w1 = ONE ? 0 : table_word<TABLE>(p, seq, i1);
     int32_t cv_word = 0;
@@ -426,9 +426,11 @@ static void launch_short_hg(const DecodeParams& p, dim3 g, bool scrub, hipStream
     const bool table = p.bt != nullptr;
     if (p.timeline) {
         if (table)
-            hipLaunchKernelGGL((decode_short_kernel<HG, false, true, true, false, ONE>), g, blk, 0, stream, p);
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, true, true, false, ONE>), g, blk, 0,
+                               stream, p);
         else
-            hipLaunchKernelGGL((decode_short_kernel<HG, false, false, true, false, ONE>), g, blk, 0, stream, p);
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, false, true, false, ONE>), g, blk,
+                               0, stream, p);
         return;
     }
     if (p.slots) {
@@ -442,14 +444,18 @@ static void launch_short_hg(const DecodeParams& p, dim3 g, bool scrub, hipStream
     }
     if (scrub) {
         if (table)
-            hipLaunchKernelGGL((decode_short_kernel<HG, true, true, false, false, ONE>), g, blk, 0, stream, p);
+            hipLaunchKernelGGL((decode_short_kernel<HG, true, true, false, false, ONE>), g, blk, 0,
+                               stream, p);
         else
-            hipLaunchKernelGGL((decode_short_kernel<HG, true, false, false, false, ONE>), g, blk, 0, stream, p);
+            hipLaunchKernelGGL((decode_short_kernel<HG, true, false, false, false, ONE>), g, blk,
+                               0, stream, p);
     } else {
         if (table)
-            hipLaunchKernelGGL((decode_short_kernel<HG, false, true, false, false, ONE>), g, blk, 0, stream, p);
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, true, false, false, ONE>), g, blk,
+                               0, stream, p);
         else
-            hipLaunchKernelGGL((decode_short_kernel<HG, false, false, false, false, ONE>), g, blk, 0, stream, p);
+            hipLaunchKernelGGL((decode_short_kernel<HG, false, false, false, false, ONE>), g, blk,
+                               0, stream, p);
     }
 }
 
